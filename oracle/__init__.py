@@ -1,0 +1,163 @@
+"""Float64 CPU oracle for bidirectional multi-head attention over packed sequences.
+
+TEST INFRASTRUCTURE ONLY.  This package is the checker the GPU path is compared
+against.  Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import it.  It shares no code with the GPU path (the HIP kernels
+and their C ABI in ``vision_transformer_attention_amd``) and imports nothing from
+it; the seeded input generator is the only module both sides use.
+
+The arithmetic lives in ``vitattn_ref.c`` (plain C, float64, libm ``exp``): for each
+sequence ``[cu[s], cu[s+1])``, head ``h`` and query row ``i`` of that sequence,
+``O[i,h,:] = sum_j softmax_j(scale * Q[i,h,:].K[j,h,:]) * V[j,h,:]`` with ``j`` over
+the same sequence only.  Sources, by page title:
+
+* "inferencelayer 0.2.1 src/vision_gpu.rs" -- vis_attn_coop_src doc, "The obstacle,
+  and the way round it" (the online-softmax update whose result is this weighted
+  average, and the final division by the row sum); ``VisionGpu::forward_one``
+  segment tables (attention stays inside one image; more images are more segments).
+* "hf2q src/inference/vision/vit_gpu.rs" -- ``vit_attention_gpu`` doc (no mask, the
+  ViT is bidirectional; seq-major ``[tokens, heads, head_dim]``) and
+  ``vit_attention_scores_gpu`` doc (the scale is the caller's, 1.0 allowed).
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
+hand-derived golden values, invariants, and a library routine (PyTorch's CPU
+``scaled_dot_product_attention`` in float64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vitattn_ref.c")
+_LIB_PATH = os.path.join(_HERE, "libvitattn_oracle.so")
+_lib = None
+
+
+def build(out_path: str | None = None, extra_cflags: tuple[str, ...] = ()) -> str:
+    """Compile the C oracle with gcc (OpenMP) into a shared library; returns its path."""
+    out = out_path or _LIB_PATH
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-Wall", *extra_cflags, _SRC, "-lm", "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.vitattn_ref_fwd_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_double]
+    lib.vitattn_ref_fwd_f64.restype = ctypes.c_int
+    lib.vitattn_ref_rows_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_double, i64p, ctypes.c_int64]
+    lib.vitattn_ref_rows_f64.restype = ctypes.c_int
+    lib.vitattn_ref_row_probs_f64.argtypes = [f32p, f32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_double, ctypes.c_int64, ctypes.c_int32, f64p]
+    lib.vitattn_ref_row_probs_f64.restype = ctypes.c_int64
+    lib.vitattn_ref_threads.argtypes = []
+    lib.vitattn_ref_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it first if it is missing)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _as_f32(x) -> np.ndarray:
+    """Inputs as contiguous float32 (exact for float32 and bfloat16 data)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.float32)
+    if a.ndim != 3:
+        raise ValueError("q/k/v must be [tokens, heads, head_dim]")
+    return a
+
+
+def _cu(cu_seqlens) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def attention(q, k, v, cu_seqlens, scale: float, lib=None) -> np.ndarray:
+    """Full float64 output ``[T, H, D]``; rows outside every sequence stay 0."""
+    lib = lib or load()
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    cu = _cu(cu_seqlens)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same shape")
+    t, h, d = q.shape
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != t or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    o = np.zeros((t, h, d), dtype=np.float64)
+    rc = lib.vitattn_ref_fwd_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                 _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, d,
+                                 float(scale))
+    if rc != 0:
+        raise RuntimeError("oracle failed")
+    return o
+
+
+def attention_rows(q, k, v, cu_seqlens, scale: float, rows, lib=None) -> np.ndarray:
+    """Float64 output for the token rows listed in ``rows`` only: ``[len(rows), H, D]``."""
+    lib = lib or load()
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    cu = _cu(cu_seqlens)
+    t, h, d = q.shape
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] != t or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    r = np.ascontiguousarray(np.asarray(rows), dtype=np.int64)
+    o = np.zeros((len(r), h, d), dtype=np.float64)
+    rc = lib.vitattn_ref_rows_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                  _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, d,
+                                  float(scale), _ptr(r, ctypes.c_int64), len(r))
+    if rc != 0:
+        raise RuntimeError("oracle failed (bad rows?)")
+    return o
+
+
+def row_probs(q, k, cu_seqlens, scale: float, row: int, head: int, lib=None) -> np.ndarray:
+    """The attention weights (float64) of one query row and head over its sequence's keys."""
+    lib = lib or load()
+    q, k = _as_f32(q), _as_f32(k)
+    cu = _cu(cu_seqlens)
+    t, h, d = q.shape
+    out = np.zeros(max(t, 1), dtype=np.float64)
+    n = lib.vitattn_ref_row_probs_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(cu, ctypes.c_int32),
+                                      len(cu) - 1, h, d, float(scale), int(row), int(head),
+                                      _ptr(out, ctypes.c_double))
+    if n < 0:
+        raise RuntimeError("oracle failed (bad row/head?)")
+    return out[:n].copy()
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel regions use."""
+    return int(load().vitattn_ref_threads())

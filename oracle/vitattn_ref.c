@@ -1,0 +1,200 @@
+/*
+ * vitattn_ref.c -- the float64 CPU oracle for bidirectional multi-head
+ * scaled-dot-product attention over packed variable-length sequences.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker that the GPU path is
+ * compared against.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline may load it; the product library never links, loads or calls it,
+ * and it shares no code, header, table or constant with the GPU path.
+ *
+ * What it computes (the plain definition, not the GPU algorithm):
+ *   For every sequence s with rows [a, b) = [cu[s], cu[s+1]), every head h and
+ *   every query row i in [a, b):
+ *     l_j   = scale * sum_{d<D} Q[i,h,d] * K[j,h,d]          for j in [a, b)
+ *     m     = max_j l_j
+ *     w_j   = exp(l_j - m)
+ *     Z     = sum_j w_j
+ *     O[i,h,e] = (sum_j w_j * V[j,h,e]) / Z                  for e < D
+ *   Keys never cross a sequence boundary (block-diagonal attention) and there
+ *   is no other mask (the attention is bidirectional).
+ *
+ * Sources (pages as titled in the reference collection):
+ *  - "inferencelayer 0.2.1 src/vision_gpu.rs", doc of vis_attn_coop_src,
+ *    section "The obstacle, and the way round it": the online update
+ *    O <- O*e^(m_old - m_new) + P*V, whose fixed point is the softmax-weighted
+ *    average written above; and the closing division of the running output by
+ *    the running row sum.
+ *  - same page, VisionGpu::forward_one, the segment tables: one image is one
+ *    ragged segment and tokens attend within their image, never across it;
+ *    several images are several segments (here: the cu_seqlens prefix array).
+ *  - "hf2q src/inference/vision/vit_gpu.rs", doc of vit_attention_gpu: full
+ *    scaled-dot-product attention with no mask because the ViT is
+ *    bidirectional; tensors are seq-major [tokens, heads, head_dim]; and doc of
+ *    vit_attention_scores_gpu: the scale is the caller's value (1/sqrt(hd) for
+ *    a standard ViT, 1.0 for Gemma 4V), with no implicit scaling.
+ *
+ * Readings taken where the pages are silent: the max is subtracted before the
+ * exponential (a two-pass softmax; mathematically the same result); the scale
+ * multiplies the dot product before the max; inputs arrive as float32 values
+ * (exact for float32 and for bfloat16 data) and every operation is float64 with
+ * libm exp; a zero-length sequence has no rows and writes nothing.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC vitattn_ref.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One query row of one head: writes D outputs to out[0..D).  `w` is caller
+ * scratch of at least (b - a) doubles. */
+static void ref_one_row(const float* q, const float* k, const float* v,
+                        int64_t a, int64_t b, int64_t i, int32_t h,
+                        int32_t n_heads, int32_t head_dim, double scale,
+                        double* w, double* out) {
+  const int64_t row_stride = (int64_t)n_heads * head_dim;
+  const float* qi = q + i * row_stride + (int64_t)h * head_dim;
+  /* pass 1: logits and their maximum */
+  double m = -INFINITY;
+  for (int64_t j = a; j < b; ++j) {
+    const float* kj = k + j * row_stride + (int64_t)h * head_dim;
+    double dot = 0.0;
+    for (int32_t d = 0; d < head_dim; ++d) dot += (double)qi[d] * (double)kj[d];
+    double logit = scale * dot;
+    w[j - a] = logit;
+    if (logit > m) m = logit;
+  }
+  /* pass 2: weights, their sum, and the weighted average of V */
+  double z = 0.0;
+  for (int64_t j = a; j < b; ++j) {
+    double wj = exp(w[j - a] - m);
+    w[j - a] = wj;
+    z += wj;
+  }
+  for (int32_t e = 0; e < head_dim; ++e) out[e] = 0.0;
+  for (int64_t j = a; j < b; ++j) {
+    const float* vj = v + j * row_stride + (int64_t)h * head_dim;
+    for (int32_t e = 0; e < head_dim; ++e) out[e] += w[j - a] * (double)vj[e];
+  }
+  for (int32_t e = 0; e < head_dim; ++e) out[e] /= z;
+}
+
+/* Number of threads an OpenMP region here will use (1 without OpenMP). */
+int vitattn_ref_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Full output o[T, H, D] (float64) for q, k, v [T, H, D] (float32 values).
+ * Returns 0, or -1 on a bad argument or an allocation failure. */
+int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* o,
+                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                        int32_t head_dim, double scale) {
+  if (n_seqs < 0 || n_heads <= 0 || head_dim <= 0) return -1;
+  if (n_seqs == 0) return 0;
+  if (!q || !k || !v || !o || !cu_seqlens) return -1;
+  int64_t max_len = 0;
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    int64_t len = (int64_t)cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len < 0) return -1;
+    if (len > max_len) max_len = len;
+  }
+  const int64_t n_pairs = (int64_t)n_seqs * n_heads;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!w) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t p = 0; p < n_pairs; ++p) {
+        int32_t s = (int32_t)(p / n_heads), h = (int32_t)(p % n_heads);
+        int64_t a = cu_seqlens[s], b = cu_seqlens[s + 1];
+        for (int64_t i = a; i < b; ++i)
+          ref_one_row(q, k, v, a, b, i, h, n_heads, head_dim, scale, w,
+                      o + (i * n_heads + h) * (int64_t)head_dim);
+      }
+      free(w);
+    }
+  }
+  return failed ? -1 : 0;
+}
+
+/* Output for a chosen set of token rows only: o_rows[n_rows, H, D] (float64),
+ * rows[r] a global token index in [0, T).  Used where the full output would
+ * take too long.  Returns 0, or -1 on a bad argument. */
+int vitattn_ref_rows_f64(const float* q, const float* k, const float* v, double* o_rows,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                         int32_t head_dim, double scale, const int64_t* rows, int64_t n_rows) {
+  if (n_seqs <= 0 || n_heads <= 0 || head_dim <= 0 || n_rows < 0) return -1;
+  if (!q || !k || !v || !o_rows || !cu_seqlens || (n_rows > 0 && !rows)) return -1;
+  const int64_t total = cu_seqlens[n_seqs];
+  int64_t max_len = 0;
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    int64_t len = (int64_t)cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len < 0) return -1;
+    if (len > max_len) max_len = len;
+  }
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= total) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!w) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t p = 0; p < n_rows * n_heads; ++p) {
+        int64_t r = p / n_heads;
+        int32_t h = (int32_t)(p % n_heads);
+        int64_t i = rows[r];
+        /* the sequence that holds row i: the last s with cu[s] <= i < cu[s+1] */
+        int32_t s = 0;
+        while (!(cu_seqlens[s] <= i && i < cu_seqlens[s + 1])) ++s;
+        ref_one_row(q, k, v, cu_seqlens[s], cu_seqlens[s + 1], i, h, n_heads, head_dim,
+                    scale, w, o_rows + (r * n_heads + h) * (int64_t)head_dim);
+      }
+      free(w);
+    }
+  }
+  return failed ? -1 : 0;
+}
+
+/* The attention weights of one (token row, head): p_out[j - a] for the keys j
+ * of the row's sequence [a, b).  Returns b - a, or -1 on a bad argument. */
+int64_t vitattn_ref_row_probs_f64(const float* q, const float* k, const int32_t* cu_seqlens,
+                                  int32_t n_seqs, int32_t n_heads, int32_t head_dim,
+                                  double scale, int64_t row, int32_t head, double* p_out) {
+  if (n_seqs <= 0 || n_heads <= 0 || head_dim <= 0 || head < 0 || head >= n_heads) return -1;
+  if (row < 0 || row >= cu_seqlens[n_seqs]) return -1;
+  int32_t s = 0;
+  while (!(cu_seqlens[s] <= row && row < cu_seqlens[s + 1])) ++s;
+  const int64_t a = cu_seqlens[s], b = cu_seqlens[s + 1];
+  const int64_t row_stride = (int64_t)n_heads * head_dim;
+  const float* qi = q + row * row_stride + (int64_t)head * head_dim;
+  double m = -INFINITY;
+  for (int64_t j = a; j < b; ++j) {
+    const float* kj = k + j * row_stride + (int64_t)head * head_dim;
+    double dot = 0.0;
+    for (int32_t d = 0; d < head_dim; ++d) dot += (double)qi[d] * (double)kj[d];
+    p_out[j - a] = scale * dot;
+    if (p_out[j - a] > m) m = p_out[j - a];
+  }
+  double z = 0.0;
+  for (int64_t j = a; j < b; ++j) {
+    p_out[j - a] = exp(p_out[j - a] - m);
+    z += p_out[j - a];
+  }
+  for (int64_t j = a; j < b; ++j) p_out[j - a] /= z;
+  return b - a;
+}

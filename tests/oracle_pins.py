@@ -1,0 +1,210 @@
+"""Checks that pin the float64 oracle to facts other than itself.
+
+Each check takes the loaded oracle library and raises AssertionError on a miss.
+They are closed forms worked out by hand (``golden/closed_forms.json``), exact
+special cases, invariants that the definition implies, and a library routine
+(PyTorch's CPU ``scaled_dot_product_attention`` in float64).  Together they are
+chosen so that a plausible slip in the oracle -- a wrong sign, a dropped scale
+or normalisation, swapped operands, a head or sequence index mix-up, an
+off-by-one over the keys -- fails at least one of them (``test_oracle_mutants``
+plants such slips and checks this).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
+_SCALES = {"ln2": math.log(2.0), "ln3": math.log(3.0), "1": 1.0}
+
+
+def _rand(lengths, h, d, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    t = int(sum(lengths))
+    q = (rng.standard_normal((t, h, d)) * std).astype(np.float32)
+    k = (rng.standard_normal((t, h, d)) * std).astype(np.float32)
+    v = rng.standard_normal((t, h, d)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def _segments(cu):
+    return [(int(cu[s]), int(cu[s + 1])) for s in range(len(cu) - 1)]
+
+
+def pin_golden(lib):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float32)
+        k = np.array(c["k"], dtype=np.float32)
+        v = np.array(c["v"], dtype=np.float32)
+        exp = np.array([[[float(Fraction(x)) for x in hv] for hv in row] for row in c["expected"]])
+        got = oracle.attention(q, k, v, c["cu_seqlens"], _SCALES[c["scale"]], lib=lib)
+        assert np.allclose(got, exp, rtol=1e-13, atol=1e-13), (c["name"], got, exp)
+
+
+def pin_scale_one_logistic(lib):
+    # scale 1.0 (the Gemma 4V choice): logits (0, 1) give weights (1, e)/(1 + e)
+    q = np.array([[[1.0]], [[0.0]]], np.float32)
+    k = np.array([[[0.0]], [[1.0]]], np.float32)
+    v = np.array([[[0.0]], [[1.0]]], np.float32)
+    got = oracle.attention(q, k, v, [0, 2], 1.0, lib=lib)
+    assert abs(got[0, 0, 0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(got[1, 0, 0] - 0.5) < 1e-15
+
+
+def pin_single_key(lib):
+    q, k, v, cu = _rand([1, 1, 1, 1], 3, 8, seed=11)
+    got = oracle.attention(q, k, v, cu, 0.37, lib=lib)
+    assert np.array_equal(got, v.astype(np.float64))
+
+
+def pin_constant_v(lib):
+    q, k, v, cu = _rand([5, 9, 2], 2, 6, seed=12, std=2.0)
+    c = np.random.default_rng(13).standard_normal((1, 2, 6)).astype(np.float32)
+    v = np.broadcast_to(c, v.shape).copy()
+    got = oracle.attention(q, k, v, cu, 0.5, lib=lib)
+    assert np.allclose(got, np.broadcast_to(c, got.shape), rtol=1e-14, atol=1e-14)
+
+
+def pin_uniform_when_no_signal(lib):
+    # Q = 0, or scale = 0: every key gets the same weight -> the sequence mean of V
+    q, k, v, cu = _rand([4, 7, 3], 2, 5, seed=14)
+    means = np.zeros(v.shape, np.float64)
+    for a, b in _segments(cu):
+        for h in range(v.shape[1]):
+            for e in range(v.shape[2]):
+                means[a:b, h, e] = math.fsum(float(x) for x in v[a:b, h, e]) / (b - a)
+    got0 = oracle.attention(np.zeros_like(q), k, v, cu, 0.9, lib=lib)
+    gots = oracle.attention(q, k, v, cu, 0.0, lib=lib)
+    assert np.allclose(got0, means, rtol=1e-14, atol=1e-14)
+    assert np.allclose(gots, means, rtol=1e-14, atol=1e-14)
+
+
+def pin_weights_are_a_distribution(lib):
+    # with V the identity over a sequence's keys, row i of the output is row i of the weights
+    L = 6
+    rng = np.random.default_rng(15)
+    q = rng.standard_normal((L, 1, L)).astype(np.float32)
+    k = rng.standard_normal((L, 1, L)).astype(np.float32)
+    v = np.eye(L, dtype=np.float32)[:, None, :]
+    got = oracle.attention(q, k, v, [0, L], 0.7, lib=lib)
+    for i in range(L):
+        p = oracle.row_probs(q, k, [0, L], 0.7, i, 0, lib=lib)
+        assert abs(math.fsum(p) - 1.0) < 1e-14
+        assert np.all(p > 0)
+        assert np.allclose(got[i, 0, :], p, rtol=1e-14, atol=1e-15)
+    # two keys: the weights are logistic in the logit difference
+    p = oracle.row_probs(q[:2], k[:2], [0, 2], 0.7, 0, 0, lib=lib)
+    d = 0.7 * (float(np.dot(q[0, 0].astype(np.float64), k[1, 0])) - float(np.dot(q[0, 0].astype(np.float64), k[0, 0])))
+    assert abs(p[0] - 1.0 / (1.0 + math.exp(d))) < 1e-14
+
+
+def pin_key_shift_invariance(lib):
+    q, k, v, cu = _rand([6, 10], 2, 4, seed=16)
+    k = (np.round(k * 64.0) / 64.0).astype(np.float32)  # coarse grid: k + u below is exact in float32
+    base = oracle.attention(q, k, v, cu, 0.6, lib=lib)
+    k2 = k.copy()
+    u = np.array([[0.5, -0.25, 1.0, 0.125], [-1.0, 0.75, 0.0, 0.5]], np.float32)  # per head, exact in f32
+    k2 += u[None]
+    got = oracle.attention(q, k2, v, cu, 0.6, lib=lib)
+    assert np.allclose(got, base, rtol=1e-12, atol=1e-12)
+
+
+def pin_key_permutation_invariance(lib):
+    q, k, v, cu = _rand([7, 5], 3, 4, seed=17)
+    base = oracle.attention(q, k, v, cu, 0.8, lib=lib)
+    perm = np.concatenate([np.random.default_rng(18).permutation(np.arange(a, b)) for a, b in _segments(cu)])
+    # permute keys and values together; queries keep their rows
+    got = oracle.attention(q, k[perm], v[perm], cu, 0.8, lib=lib)
+    assert np.allclose(got, base, rtol=1e-13, atol=1e-13)
+
+
+def pin_affine_in_v(lib):
+    q, k, v, cu = _rand([8, 3], 2, 3, seed=19)
+    v = (np.round(v * 64.0) / 64.0).astype(np.float32)  # coarse grid: 2v + 3 is exact in float32
+    base = oracle.attention(q, k, v, cu, 0.5, lib=lib)
+    got = oracle.attention(q, k, (2.0 * v + 3.0).astype(np.float32), cu, 0.5, lib=lib)
+    assert np.allclose(got, 2.0 * base + 3.0, rtol=1e-13, atol=1e-13)
+
+
+def pin_convex_hull(lib):
+    q, k, v, cu = _rand([9, 4, 1], 2, 5, seed=20, std=3.0)
+    got = oracle.attention(q, k, v, cu, 1.0, lib=lib)
+    for a, b in _segments(cu):
+        lo = v[a:b].min(axis=0).astype(np.float64)
+        hi = v[a:b].max(axis=0).astype(np.float64)
+        assert np.all(got[a:b] >= lo[None] - 1e-12) and np.all(got[a:b] <= hi[None] + 1e-12)
+
+
+def pin_block_diagonal(lib):
+    lengths = [5, 1, 8, 3]
+    q, k, v, cu = _rand(lengths, 2, 4, seed=21)
+    packed = oracle.attention(q, k, v, cu, 0.7, lib=lib)
+    for a, b in _segments(cu):
+        alone = oracle.attention(q[a:b], k[a:b], v[a:b], [0, b - a], 0.7, lib=lib)
+        assert np.array_equal(alone, packed[a:b])
+    # reordering the images reorders the output and changes nothing else
+    order = [2, 0, 3, 1]
+    segs = _segments(cu)
+    idx = np.concatenate([np.arange(*segs[s]) for s in order])
+    cu2 = np.concatenate([[0], np.cumsum([lengths[s] for s in order])]).astype(np.int32)
+    re = oracle.attention(q[idx], k[idx], v[idx], cu2, 0.7, lib=lib)
+    assert np.array_equal(re, packed[idx])
+
+
+def pin_head_independence(lib):
+    q, k, v, cu = _rand([6, 4], 3, 4, seed=22)
+    base = oracle.attention(q, k, v, cu, 0.7, lib=lib)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, 1] += 1.0
+    k2[:, 1] *= -2.0
+    v2[:, 1] += 5.0
+    got = oracle.attention(q2, k2, v2, cu, 0.7, lib=lib)
+    assert np.array_equal(got[:, 0], base[:, 0]) and np.array_equal(got[:, 2], base[:, 2])
+    assert not np.allclose(got[:, 1], base[:, 1])
+
+
+def pin_head_dim_zero_padding(lib):
+    q, k, v, cu = _rand([5, 6], 2, 3, seed=23)
+    base = oracle.attention(q, k, v, cu, 0.45, lib=lib)
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:2] + (5,), np.float32)], axis=2)
+    got = oracle.attention(pad(q), pad(k), pad(v), cu, 0.45, lib=lib)
+    assert np.array_equal(got[:, :, :3], base) and np.all(got[:, :, 3:] == 0.0)
+
+
+def pin_torch_sdpa(lib):
+    # a library routine computing the same definition: PyTorch CPU SDPA in float64, per image
+    import torch
+    import torch.nn.functional as F
+    lengths = [33, 1, 70, 17]
+    q, k, v, cu = _rand(lengths, 4, 24, seed=24, std=1.5)
+    got = oracle.attention(q, k, v, cu, 0.31, lib=lib)
+    for a, b in _segments(cu):
+        t = lambda x: torch.from_numpy(x[a:b].astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+        ref = F.scaled_dot_product_attention(t(q), t(k), t(v), scale=0.31)
+        ref = ref.squeeze(0).permute(1, 0, 2).numpy()
+        assert np.allclose(got[a:b], ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_rows_match_full(lib):
+    q, k, v, cu = _rand([12, 5, 9], 2, 6, seed=25)
+    full = oracle.attention(q, k, v, cu, 0.4, lib=lib)
+    rows = np.array([0, 11, 12, 16, 17, 25, 3], np.int64)
+    got = oracle.attention_rows(q, k, v, cu, 0.4, rows, lib=lib)
+    assert np.array_equal(got, full[rows])
+
+
+PINS = [
+    pin_golden, pin_scale_one_logistic, pin_single_key, pin_constant_v, pin_uniform_when_no_signal,
+    pin_weights_are_a_distribution, pin_key_shift_invariance, pin_key_permutation_invariance,
+    pin_affine_in_v, pin_convex_hull, pin_block_diagonal, pin_head_independence,
+    pin_head_dim_zero_padding, pin_torch_sdpa, pin_rows_match_full,
+]

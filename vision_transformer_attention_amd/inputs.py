@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the GPU path's tests and benchmark and by the float64
+oracle's tests.  It only draws random numbers and lays them out; it holds none
+of the attention arithmetic.
+
+Recipe (every workload): ``numpy.random.default_rng(seed)`` (PCG64) draws float32
+``standard_normal`` arrays in the fixed order Q, K, V, each ``[T, H, D]`` row-major
+(seq-major tokens, then heads, then head_dim), then any per-token factors.  bf16
+tensors are the float32 draws rounded to nearest-even by ``torch.Tensor.to``.
+The sequence-length prefix array ``cu_seqlens`` is int32 ``[n_seqs + 1]``.
+
+The shapes follow the pages' vision-tower workloads: a 196-patch image at hidden
+1152 (16 heads of 72), a 912-patch document page at 16 heads, several images
+packed into one call, and a long high-resolution sequence.  The pages measured on
+private images with trained weights; these seeded tensors of the same shapes
+stand in for them.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    lengths: tuple[int, ...]
+    n_heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+    std: float = 1.0
+    token_factor: tuple[float, float] | None = None  # uniform per-token factor on Q and K
+    scale: float | None = None  # None -> 1/sqrt(head_dim)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.lengths))
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def flops(self) -> int:
+        """4 * sum_s L_s^2 * D * H: two matmuls of 2*L*L*D flops per head and sequence."""
+        return 4 * sum(l * l for l in self.lengths) * self.head_dim * self.n_heads
+
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+
+
+# The lengths of the packed batch are numpy.random.default_rng(17).integers(256, 4097, 8),
+# written out so that the workload does not depend on numpy's stream staying stable.
+PACKED_LENGTHS = (3102, 3501, 668, 874, 2015, 2398, 3181, 1669)
+
+WORKLOADS: dict[str, Workload] = {
+    "tiny-64": Workload("tiny-64", (64,), 4, 64, F32, seed=1, scale=1.0 / 8.0),
+    "vit-196": Workload("vit-196", (196,), 16, 72, BF16, seed=2, std=0.5),
+    "page-912": Workload("page-912", (912,), 16, 80, BF16, seed=3, token_factor=(0.5, 2.0)),
+    "packed-varlen-8": Workload("packed-varlen-8", PACKED_LENGTHS, 16, 80, BF16, seed=4),
+    "long-16384": Workload("long-16384", (16384,), 16, 128, BF16, seed=5),
+}
+
+
+def custom(lengths, n_heads: int, head_dim: int, dtype: str = BF16, seed: int = 0, std: float = 1.0,
+           token_factor=None, scale: float | None = None, name: str = "custom") -> Workload:
+    return Workload(name, tuple(int(x) for x in lengths), int(n_heads), int(head_dim), dtype, int(seed),
+                    float(std), token_factor, scale)
+
+
+def draw_f32(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The float32 draws (before any bf16 rounding), each ``[T, H, D]``."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.total_tokens, w.n_heads, w.head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if w.std != 1.0:
+        s = np.float32(w.std)
+        q *= s
+        k *= s
+        v *= s
+    if w.token_factor is not None:
+        lo, hi = w.token_factor
+        fq = rng.uniform(lo, hi, size=w.total_tokens).astype(np.float32)
+        fk = rng.uniform(lo, hi, size=w.total_tokens).astype(np.float32)
+        q *= fq[:, None, None]
+        k *= fk[:, None, None]
+    return q, k, v
+
+
+def make(w: Workload | str):
+    """(q, k, v, cu_seqlens, scale) as CPU torch tensors in the workload's dtype."""
+    import torch
+
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    q, k, v = draw_f32(w)
+    tdt = torch.float32 if w.dtype == F32 else torch.bfloat16
+    qt, kt, vt = (torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
+    cu = torch.from_numpy(w.cu_seqlens())
+    return qt, kt, vt, cu, w.softmax_scale

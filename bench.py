@@ -1,0 +1,175 @@
+"""Benchmark: attention TFLOP/s of the HIP path on one MI355X.
+
+One step is one ``vitattn_fwd`` call (the whole hot path: work planning, K/V
+staging, both MFMA products, online softmax and the epilogue) over one batch of
+seeded synthetic input.  The headline workload is the packed variable-length
+batch (8 images, 17,408 tokens, 16 heads of 80, bf16); the 912-patch page
+(16 heads of 80, bf16), also named by the metric, is timed beside it.  FLOPs are
+4 * sum_s L_s^2 * D * H with the true head_dim.  Inputs are resident in HBM before
+the timed region starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+HEADLINE = "packed-varlen-8"
+SECONDARY = "page-912"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_workload(name: str, steps: int, warmup: int):
+    import torch
+
+    import vision_transformer_attention_amd as vta
+    from vision_transformer_attention_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    q, k, v, cu, scale = inputs.make(w)
+    dev = torch.device("cuda:0")
+    q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = start.elapsed_time(end) / steps  # events on the launch stream
+    cfg = vta.binding.kernel_config(w.head_dim, q.dtype)
+    return w, kernel_ms, wall * 1e3 / steps, cfg
+
+
+def cpu_baseline(name: str, target_s: float = 12.0):
+    """The float64 oracle timed on the host's cores on a bounded sample of query rows."""
+    import numpy as np
+
+    import oracle
+    from vision_transformer_attention_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    q, k, v, cu, scale = inputs.make(w)
+    cu_np = cu.numpy()
+    lens = np.diff(cu_np)
+    seq_of = np.repeat(np.arange(len(lens)), lens)
+    rng = np.random.default_rng(123)
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(w.total_tokens, size=n_rows, replace=False)).astype(np.int64)
+        flops = float(np.sum(4.0 * lens[seq_of[rows]] * w.head_dim * w.n_heads))
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, cu, scale, rows)
+        return time.perf_counter() - t0, flops, n_rows
+
+    dt, fl, n = run(16)
+    per_row = max(dt / n, 1e-6)
+    n_rows = int(min(w.total_tokens, max(16, target_s / per_row)))
+    dt, fl, n = run(n_rows)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {w.total_tokens} query rows of {name} (all 16 heads, every key of each row's image), "
+                  f"float64, {dt:.1f} s",
+    }
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if present and current."""
+    path = os.path.join(PROFILES, f"attn_fwd_bf16_d80_{name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=HEADLINE)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path here is a "
+              f"single-GPU build, see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup)
+    tflops = w.flops / (kernel_ms * 1e-3) / 1e12
+    log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    sec = None
+    if args.workload != SECONDARY:
+        log(f"[bench] timing {SECONDARY}")
+        w2, k2, wall2, cfg2 = time_workload(SECONDARY, max(args.steps, 200), args.warmup)
+        sec = {"workload": SECONDARY, "value": w2.flops / (k2 * 1e-3) / 1e12, "unit": "TFLOP/s",
+               "ms_per_step": k2, "frac_of_bf16_peak": w2.flops / (k2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        log(f"[bench] {SECONDARY}: {k2 * 1e3:.1f} us/launch, {sec['value']:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host cores (bounded sample)")
+        cpu = cpu_baseline(args.workload)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    dtype = "bf16" if w.dtype == "bf16" else "f32"
+    rec = {
+        "metric": "attention TFLOP/s (4*S^2*D*H summed over sequences)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": kernel_ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {
+            "workload": w.name, "lengths": list(w.lengths), "tokens": w.total_tokens, "heads": w.n_heads,
+            "head_dim": w.head_dim, "flops_per_step": w.flops, "block_m": cfg["block_m"],
+            "block_n": cfg["block_n"], "waves_per_workgroup": cfg["waves"], "grid": cfg["grid"],
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / BF16_PEAK_TFLOPS, "traffic": load_traffic(w.name),
+        },
+        "secondary": sec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,108 @@
+/*
+ * vitattn.h -- C ABI of libvitattn, bidirectional multi-head attention for
+ * vision-transformer encoders on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (by page title in the reference collection):
+ *  - "hf2q src/inference/vision/vit_gpu.rs", doc of vit_attention_gpu: full
+ *    scaled-dot-product attention with no mask, because a ViT encoder is
+ *    bidirectional; Q, K, V and the output are seq-major
+ *    [tokens, heads, head_dim].  Doc of vit_attention_scores_gpu: the scale
+ *    multiplying Q.K^T is the caller's value (1/sqrt(head_dim) for a standard
+ *    ViT, 1.0 for Gemma 4V); nothing is scaled implicitly.
+ *  - "inferencelayer 0.2.1 src/vision_gpu.rs", VisionGpu::forward_one, the
+ *    segment tables: a token attends within its own image and never across;
+ *    batching several images is several segments.  Here the segments are the
+ *    prefix array cu_seqlens.
+ *  - same page, doc of vis_attn_coop_src ("The obstacle, and the way round
+ *    it"): the online-softmax recurrence O <- O*e^(m_old-m_new) + P.V over key
+ *    tiles, finished by dividing by the running row sum -- the algorithm the
+ *    kernels use to reach the result without materialising the scores.
+ *
+ * For every sequence s in [0, n_seqs), every head h and every token row
+ * i in [cu_seqlens[s], cu_seqlens[s+1]):
+ *     o[i,h,:] = sum_j softmax_j(scale * q[i,h,:] . k[j,h,:]) * v[j,h,:]
+ * with j over the same range [cu_seqlens[s], cu_seqlens[s+1]).
+ */
+#ifndef VITATTN_H
+#define VITATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o (all four share it). */
+typedef enum {
+  VITATTN_DTYPE_F32 = 0,  /* IEEE float32; computed in float32 (float32 MFMA) */
+  VITATTN_DTYPE_BF16 = 1  /* bfloat16; bf16 MFMA products, float32 accumulation,
+                             output rounded to nearest even */
+} vitattn_dtype_t;
+
+/* Status codes.  Every entry point returns one of these. */
+typedef enum {
+  VITATTN_OK = 0,
+  VITATTN_ERR_INVALID_ARG = -1,           /* null/misaligned pointer, bad count, non-finite scale */
+  VITATTN_ERR_UNSUPPORTED_HEAD_DIM = -2,  /* head_dim not in {64, 72, 80, 128} */
+  VITATTN_ERR_UNSUPPORTED_DTYPE = -3,     /* dtype not a vitattn_dtype_t value */
+  VITATTN_ERR_NO_DEVICE = -4,             /* no HIP device, or the current one is not gfx950 */
+  VITATTN_ERR_OOM = -5,                   /* reserved: the forward pass allocates nothing */
+  VITATTN_ERR_HIP = -6                    /* a HIP runtime call or kernel launch failed */
+} vitattn_status_t;
+
+/*
+ * vitattn_fwd -- enqueue one attention forward pass on `stream`.
+ *
+ * q, k, v : DEVICE pointers, contiguous [T, n_heads, head_dim] of `dtype`,
+ *           T = cu_seqlens[n_seqs].  16-byte aligned.  Read only.
+ * o       : DEVICE pointer, contiguous [T, n_heads, head_dim] of `dtype`,
+ *           16-byte aligned, must not overlap q, k or v.  Every row that lies
+ *           in some sequence is written; nothing else is.
+ * cu_seqlens : DEVICE pointer to int32[n_seqs + 1]: cu_seqlens[0] is the
+ *           first token row, the array is non-decreasing and sequence s owns
+ *           rows [cu_seqlens[s], cu_seqlens[s+1]).  Zero-length sequences are
+ *           allowed and produce nothing.  This is a precondition the library
+ *           does not check (it never reads device memory on the host); the
+ *           Python binding checks it.
+ * n_seqs  : number of sequences (images), >= 0.  0 enqueues nothing.
+ * n_heads : > 0.  head_dim : 64, 72, 80 or 128.
+ * scale   : finite; multiplies q.k before the softmax (1/sqrt(head_dim) for a
+ *           standard ViT; 1.0 is valid).
+ * dtype   : a vitattn_dtype_t.
+ * stream  : HIP stream to enqueue on (0 = the legacy default stream).
+ *
+ * Arguments are validated before any HIP call.  The call does not
+ * synchronise the host, allocates no device memory and is safe to call from
+ * several host threads on different streams.  The library never prints,
+ * aborts or computes anything on the CPU: a failure is a status code plus a
+ * message in vitattn_last_error().  Results are bitwise reproducible for the
+ * same inputs and device.
+ */
+int vitattn_fwd(const void* q, const void* k, const void* v, void* o,
+                const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                int32_t head_dim, float scale, int32_t dtype, hipStream_t stream);
+
+/* Static, never-NULL description of a status code. */
+const char* vitattn_status_string(int status);
+
+/* Thread-local detail of the last failure on this host thread ("" if none). */
+const char* vitattn_last_error(void);
+
+/*
+ * vitattn_kernel_config -- describe the launch that vitattn_fwd makes for a
+ * (head_dim, dtype) pair on the current device, without launching anything.
+ * Writes the queries per work item (*block_m), the keys per LDS tile
+ * (*block_n), the wavefronts per workgroup (*waves) and the persistent grid
+ * size (*grid, workgroups).  Any output pointer may be NULL.  Returns a
+ * status code (the same argument errors as vitattn_fwd; NO_DEVICE or HIP if
+ * the device cannot be queried).
+ */
+int vitattn_kernel_config(int32_t head_dim, int32_t dtype, int32_t* block_m,
+                          int32_t* block_n, int32_t* waves, int32_t* grid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VITATTN_H */

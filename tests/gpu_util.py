@@ -1,0 +1,81 @@
+"""Helpers shared by the GPU tests: run the HIP path and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import vision_transformer_attention_amd as vta
+from vision_transformer_attention_amd import inputs
+
+TOL = {inputs.F32: 1e-4, inputs.BF16: 2e-2}
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(q, k, v, cu, scale, stream=None):
+    d = torch.device(DEV)
+    qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
+    if stream is None:
+        o = vta.fwd(qd, kd, vd, cud, scale)
+    else:
+        with torch.cuda.stream(stream):
+            o = vta.fwd(qd, kd, vd, cud, scale)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def max_abs_err(o_gpu, ref, rows=None) -> tuple[float, tuple]:
+    g = o_gpu.float().numpy().astype(np.float64)
+    if rows is not None:
+        g = g[np.asarray(rows)]
+    diff = np.abs(g - ref)
+    if diff.size == 0:
+        return 0.0, ()
+    idx = np.unravel_index(int(np.argmax(diff)), diff.shape)
+    return float(diff[idx]), tuple(int(x) for x in idx)
+
+
+def sample_rows(cu: np.ndarray, bm: int = 128, extra: int = 6, seed: int = 0) -> np.ndarray:
+    """Rows that exercise every sequence's edges and tile boundaries, plus a few random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        for r in (a, a + 1, b - 2, b - 1):
+            if a <= r < b:
+                rows.add(r)
+        for t in range(a + bm, b, bm * 4):
+            for r in (t - 1, t):
+                if a <= r < b:
+                    rows.add(r)
+        rows.update(int(x) for x in rng.integers(a, b, size=min(extra, b - a)))
+    return np.array(sorted(rows), np.int64)
+
+
+def check_workload(w: inputs.Workload, full: bool, rows=None):
+    say(f"[parity] {w.name}: lengths={list(w.lengths)[:10]}{'...' if len(w.lengths) > 10 else ''} "
+        f"H={w.n_heads} D={w.head_dim} {w.dtype} seed={w.seed} full={full}")
+    q, k, v, cu, scale = inputs.make(w)
+    o = run_gpu(q, k, v, cu, scale)
+    assert torch.isfinite(o.float()).all()
+    if full:
+        ref = oracle.attention(q, k, v, cu, scale)
+        err, where = max_abs_err(o, ref)
+    else:
+        if rows is None:
+            rows = sample_rows(cu.numpy())
+        ref = oracle.attention_rows(q, k, v, cu, scale, rows)
+        err, where = max_abs_err(o, ref, rows)
+    say(f"[parity] {w.name}: max-abs err {err:.3e} at {where} (tol {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype], (w.name, err, where)
+    return o, err

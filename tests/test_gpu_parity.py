@@ -1,0 +1,122 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Tolerances: max-abs 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs.
+The small workloads are compared in full; the packed batch and the long
+sequence (full size, same launch as the benchmark) on sampled rows that cover
+every image's first and last rows and tile boundaries, plus properties that hold
+at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, check_workload, run_gpu, say, sample_rows
+from vision_transformer_attention_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny-64", "vit-196", "page-912"])
+def test_workload_full(name):
+    check_workload(inputs.WORKLOADS[name], full=True)
+
+
+def test_packed_varlen_sampled_rows():
+    check_workload(inputs.WORKLOADS["packed-varlen-8"], full=False)
+
+
+def test_long_sequence_sampled_rows_and_convex_hull():
+    w = inputs.WORKLOADS["long-16384"]
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, 8191, 8192, 16382, 16383],
+                                     rng.integers(0, 16384, 23)])).astype(np.int64)
+    o, _ = check_workload(w, full=False, rows=rows)
+    _, _, v, _, _ = inputs.make(w)
+    vf, of = v.float(), o.float()
+    lo, hi = vf.min(dim=0).values, vf.max(dim=0).values
+    assert bool((of >= lo - 2e-2).all()) and bool((of <= hi + 2e-2).all())
+
+
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.F32])
+@pytest.mark.parametrize("head_dim", [64, 72, 80, 128])
+def test_edge_lengths(dtype, head_dim):
+    lengths = [1, 2, 63, 64, 65, 127, 128, 129, 255, 300]
+    w = inputs.custom(lengths, n_heads=3, head_dim=head_dim, dtype=dtype, seed=100 + head_dim)
+    check_workload(w, full=True)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0, -0.3, 2.5])
+def test_scale_is_passed_through(scale):
+    w = inputs.custom([77, 200], n_heads=2, head_dim=64, dtype=inputs.BF16, seed=9, std=0.7, scale=scale)
+    check_workload(w, full=True)
+
+
+def test_zero_length_sequences_between():
+    w = inputs.custom([0, 40, 0, 0, 129, 1, 0], n_heads=2, head_dim=80, dtype=inputs.BF16, seed=11)
+    check_workload(w, full=True)
+
+
+def test_many_sequences_unsorted_and_split_launches():
+    rng = np.random.default_rng(12)
+    lengths = rng.integers(0, 40, size=700).tolist()  # > 512 sequences: several launches
+    w = inputs.custom(lengths, n_heads=2, head_dim=72, dtype=inputs.BF16, seed=12)
+    check_workload(w, full=True)
+
+
+def test_empty_batch_is_a_noop():
+    d = torch.device("cuda:0")
+    q = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=d)
+    o = __import__("vision_transformer_attention_amd").fwd(q, q, q, torch.zeros(1, dtype=torch.int32, device=d))
+    assert o.shape == q.shape
+
+
+def test_packed_equals_each_image_alone_bitwise():
+    w = inputs.custom([300, 1, 129, 64, 513], n_heads=4, head_dim=80, dtype=inputs.BF16, seed=13)
+    q, k, v, cu, scale = inputs.make(w)
+    packed = run_gpu(q, k, v, cu, scale)
+    c = cu.numpy()
+    for s in range(len(c) - 1):
+        a, b = int(c[s]), int(c[s + 1])
+        alone = run_gpu(q[a:b].contiguous(), k[a:b].contiguous(), v[a:b].contiguous(),
+                        torch.tensor([0, b - a], dtype=torch.int32), scale)
+        assert torch.equal(alone, packed[a:b]), s
+
+
+def test_head_independence_bitwise():
+    w = inputs.custom([200, 77], n_heads=3, head_dim=64, dtype=inputs.BF16, seed=14)
+    q, k, v, cu, scale = inputs.make(w)
+    base = run_gpu(q, k, v, cu, scale)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:, 1] = -q2[:, 1]
+    k2[:, 1] = k2[:, 1] * 2
+    v2[:, 1] = v2[:, 1] + 1
+    got = run_gpu(q2, k2, v2, cu, scale)
+    assert torch.equal(got[:, 0], base[:, 0]) and torch.equal(got[:, 2], base[:, 2])
+
+
+def test_deterministic_bitwise():
+    w = inputs.WORKLOADS["page-912"]
+    q, k, v, cu, scale = inputs.make(w)
+    a = run_gpu(q, k, v, cu, scale)
+    b = run_gpu(q, k, v, cu, scale)
+    assert torch.equal(a, b)
+
+
+def test_non_default_stream_and_no_host_sync_needed():
+    w = inputs.custom([500, 33], n_heads=2, head_dim=128, dtype=inputs.BF16, seed=15)
+    q, k, v, cu, scale = inputs.make(w)
+    s = torch.cuda.Stream()
+    o = run_gpu(q, k, v, cu, scale, stream=s)
+    ref = oracle.attention(q, k, v, cu, scale)
+    err = float(np.max(np.abs(o.float().numpy() - ref)))
+    say(f"[parity] non-default stream: max-abs err {err:.3e}")
+    assert err <= TOL[inputs.BF16]
+
+
+def test_constant_v_gives_constant_output():
+    w = inputs.custom([1000], n_heads=2, head_dim=80, dtype=inputs.BF16, seed=16)
+    q, k, v, cu, scale = inputs.make(w)
+    v = torch.full_like(v, 1.5)
+    o = run_gpu(q, k, v, cu, scale)
+    assert float((o.float() - 1.5).abs().max()) <= 1e-2

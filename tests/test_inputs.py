@@ -1,0 +1,50 @@
+"""The seeded input generator: determinism, shapes, the recorded packed lengths, bf16 rounding."""
+import numpy as np
+import torch
+
+from vision_transformer_attention_amd import inputs
+
+
+def test_packed_lengths_are_the_seeded_draw():
+    assert list(np.random.default_rng(17).integers(256, 4097, 8)) == list(inputs.PACKED_LENGTHS)
+    w = inputs.WORKLOADS["packed-varlen-8"]
+    assert w.total_tokens == 17408
+    assert list(w.cu_seqlens()) == [0, 3102, 6603, 7271, 8145, 10160, 12558, 15739, 17408]
+    assert sum(l * l for l in w.lengths) == 45804456
+
+
+def test_flop_counts():
+    assert inputs.WORKLOADS["page-912"].flops == 4 * 912 * 912 * 80 * 16
+    assert inputs.WORKLOADS["packed-varlen-8"].flops == 4 * 45804456 * 80 * 16
+
+
+def test_deterministic_and_shaped():
+    for name in ("tiny-64", "vit-196", "page-912"):
+        w = inputs.WORKLOADS[name]
+        q1, k1, v1, cu1, s1 = inputs.make(w)
+        q2, k2, v2, cu2, s2 = inputs.make(w)
+        assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v1, v2) and torch.equal(cu1, cu2)
+        assert q1.shape == (w.total_tokens, w.n_heads, w.head_dim)
+        assert q1.dtype == (torch.float32 if w.dtype == inputs.F32 else torch.bfloat16)
+        assert cu1.dtype == torch.int32 and int(cu1[-1]) == w.total_tokens
+        assert s1 == w.softmax_scale
+    assert inputs.WORKLOADS["tiny-64"].softmax_scale == 1.0 / 8.0
+
+
+def test_bf16_is_round_to_nearest_even_of_the_f32_draw():
+    w = inputs.WORKLOADS["vit-196"]
+    qf, _, _ = inputs.draw_f32(w)
+    q, _, _, _, _ = inputs.make(w)
+    back = q.float().numpy()
+    # bf16 keeps the top 16 bits; RNE error is at most half a bf16 ulp
+    ulp = np.abs(qf).view(np.uint32) & 0x7F800000
+    half_ulp = (ulp.view(np.float32)) * 2.0 ** -8
+    assert np.all(np.abs(back - qf) <= half_ulp + 1e-30)
+    assert torch.equal(q.float().to(torch.bfloat16), q)
+
+
+def test_page_workload_widens_logits():
+    w = inputs.WORKLOADS["page-912"]
+    q, k, _ = inputs.draw_f32(w)
+    norms = np.linalg.norm(q.reshape(q.shape[0], -1), axis=1) / np.sqrt(q.shape[1] * q.shape[2])
+    assert norms.min() < 0.7 and norms.max() > 1.6

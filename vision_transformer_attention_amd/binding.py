@@ -1,0 +1,160 @@
+"""Thin ctypes binding over ``libvitattn.so`` (argument marshalling only).
+
+Every step of the attention runs in the HIP library; this module checks the
+torch tensors' shapes, dtypes, devices and layout, then passes raw device
+pointers and the current HIP stream to ``vitattn_fwd``.  There is no fallback:
+if the library is missing or the call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libvitattn.so"
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+HEAD_DIMS = (64, 72, 80, 128)
+
+_lib = None
+
+
+class VitattnError(RuntimeError):
+    """A non-zero status from the HIP library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"vitattn status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library(path: str | None = None):
+    """Load ``libvitattn.so`` (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise VitattnError(-100, f"{p} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.vitattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, i32, vp]
+    lib.vitattn_fwd.restype = ctypes.c_int
+    lib.vitattn_status_string.argtypes = [ctypes.c_int]
+    lib.vitattn_status_string.restype = ctypes.c_char_p
+    lib.vitattn_last_error.argtypes = []
+    lib.vitattn_last_error.restype = ctypes.c_char_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.vitattn_kernel_config.argtypes = [i32, i32, i32p, i32p, i32p, i32p]
+    lib.vitattn_kernel_config.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int) -> None:
+    if status != 0:
+        detail = lib.vitattn_last_error().decode(errors="replace")
+        name = lib.vitattn_status_string(status).decode(errors="replace")
+        raise VitattnError(status, f"{name}: {detail}")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def check_cu_seqlens(cu_host, total_tokens: int) -> None:
+    """Host-side check of the cu_seqlens precondition (int32, starts at 0, non-decreasing, ends at T)."""
+    import numpy as np
+    a = np.asarray(cu_host)
+    if a.ndim != 1 or len(a) < 1:
+        raise ValueError("cu_seqlens must be a 1-D array of n_seqs + 1 entries")
+    if a[0] != 0:
+        raise ValueError("cu_seqlens[0] must be 0")
+    if np.any(np.diff(a.astype(np.int64)) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if int(a[-1]) != total_tokens:
+        raise ValueError(f"cu_seqlens[-1] = {int(a[-1])} must equal the token count {total_tokens}")
+
+
+def kernel_config(head_dim: int, dtype) -> dict:
+    """The launch ``vitattn_fwd`` makes for (head_dim, dtype) on the current device."""
+    import torch
+    lib = load_library()
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32 if dtype == torch.float32 else -1
+    vals = [ctypes.c_int32(0) for _ in range(4)]
+    _check(lib, lib.vitattn_kernel_config(head_dim, code, *[ctypes.byref(x) for x in vals]))
+    return dict(zip(("block_m", "block_n", "waves", "grid"), (x.value for x in vals)))
+
+
+def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_seqs: int, n_heads: int,
+            head_dim: int, scale: float, dtype_code: int, stream: int) -> None:
+    """Direct call of the C entry point with raw pointers (no checks beyond the library's)."""
+    lib = load_library()
+    _check(lib, lib.vitattn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, cu_ptr, n_seqs, n_heads, head_dim,
+                                ctypes.c_float(scale), dtype_code, stream))
+
+
+def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True):
+    """Bidirectional attention over packed sequences; returns ``o`` like ``q``.
+
+    q, k, v: contiguous CUDA (HIP) tensors ``[T, H, D]`` of one dtype (bfloat16 or
+    float32), D in {64, 72, 80, 128}.  cu_seqlens: int32 ``[n_seqs + 1]`` prefix
+    array on the same device (a CPU copy is checked on the host when
+    ``check_cu``).  scale defaults to ``1/sqrt(D)``; any finite value (1.0
+    included) is passed through unchanged.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must have the same dtype")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k and v must be on the same device")
+    code = _dtype_code(q)
+    t_tokens, n_heads, head_dim = q.shape
+    if head_dim not in HEAD_DIMS:
+        raise ValueError(f"head_dim {head_dim} not in {HEAD_DIMS}")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 torch tensor")
+    if check_cu:
+        check_cu_seqlens(cu_seqlens.cpu().numpy(), t_tokens)
+    cu_dev = cu_seqlens if cu_seqlens.device == q.device else cu_seqlens.to(q.device)
+    if not cu_dev.is_contiguous():
+        cu_dev = cu_dev.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    if not math.isfinite(scale):
+        raise ValueError("scale must be finite")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    n_seqs = cu_dev.numel() - 1
+    if t_tokens == 0 or n_seqs == 0:
+        return out
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs, n_heads,
+                head_dim, float(scale), code, stream)
+    return out

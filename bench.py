@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-secondary", action="store_true", help="time only --workload (for profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path here is a "
@@ -129,8 +132,17 @@ def main():
     w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup)
     tflops = w.flops / (kernel_ms * 1e-3) / 1e12
     log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written once")
+        del src, dst
     sec = None
-    if args.workload != SECONDARY:
+    if args.workload != SECONDARY and not args.no_secondary:
         log(f"[bench] timing {SECONDARY}")
         w2, k2, wall2, cfg2 = time_workload(SECONDARY, max(args.steps, 200), args.warmup)
         sec = {"workload": SECONDARY, "value": w2.flops / (k2 * 1e-3) / 1e12, "unit": "TFLOP/s",

@@ -159,176 +159,6 @@ __device__ __forceinline__ Item map_item(const PlanLds& P, int n, int it, int bm
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
-// bf16 inputs: v_mfma_f32_16x16x32_bf16 for both products.
-template <int D_, int QB_, int NW_, int BN_>
-struct Bf16Traits {
-  using elem_t = __bf16;
-  static constexpr int D = D_, QB = QB_, NW = NW_, BN = BN_;
-  static constexpr int NT = NW * 64;
-  static constexpr int NQ = QB * 16;            // queries per wavefront
-  static constexpr int BM = NW * NQ;            // queries per item
-  static constexpr int DK = (D + 31) / 32 * 32; // Q.K^T contraction, padded
-  static constexpr int NKS = DK / 32;
-  static constexpr int DV = (D + 15) / 16 * 16; // output rows of O^T, padded
-  static constexpr int NDB = DV / 16;
-  static constexpr int NKB = BN / 16;
-  static constexpr int NKC = BN / 32;
-  static constexpr int KSTR = DK + 8;           // LDS row stride of K (elements)
-  static constexpr int VSTR = BN + 8;           // LDS row stride of V^T (elements)
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int STAGE_ELEMS = K_ELEMS + DV * VSTR;
-  static constexpr int CH = D / 8;              // 16-byte chunks per row
-  static constexpr int K_UNITS = BN * CH;
-  static constexpr int V_UNITS = (BN / 4) * CH; // 4 keys x 8 dims each
-  static constexpr int K_IT = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_IT = (V_UNITS + NT - 1) / NT;
-  static_assert(D % 8 == 0 && BN % 32 == 0, "tile shape");
-
-  struct QOp { bf16x8_t x[QB][NKS]; };
-  struct Pre { u32x4_t k[K_IT]; u32x4_t v[V_IT][4]; };
-
-  static __device__ __forceinline__ void load_q(QOp& Q, const elem_t* __restrict__ q, int row0, int qend,
-                                                int head, int n_heads, bool negate, int lane) {
-    const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = row0 + qb * 16 + c;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int d0 = ks * 32 + 8 * g;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (row < qend && d0 < D) w = ld16(q + ((size_t)row * n_heads + head) * D + d0);
-        if (negate) w ^= 0x80008000u;
-        Q.x[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void zero_pad(elem_t* stage) {
-    // K columns D..DK-1 of every row, both buffers; never written afterwards.
-    if constexpr (DK > D) {
-      constexpr int PADW = DK - D;
-      for (int i = threadIdx.x; i < 2 * BN * PADW; i += NT) {
-        const int buf = i / (BN * PADW), rem = i % (BN * PADW);
-        stage[buf * STAGE_ELEMS + (rem / PADW) * KSTR + D + rem % PADW] = (elem_t)0.0f;
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void fetch(Pre& R, const elem_t* __restrict__ k, const elem_t* __restrict__ v,
-                                               int key0, int b, int head, int n_heads) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int u = tid + i * NT;
-      R.k[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (u < K_UNITS) {
-        const int key = key0 + u / CH;
-        if (key < b) R.k[i] = ld16(k + ((size_t)key * n_heads + head) * D + (u % CH) * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * NT;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) R.v[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (u < V_UNITS) {
-        const int kbase = key0 + (u / CH) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (kbase + j < b) R.v[i][j] = ld16(v + ((size_t)(kbase + j) * n_heads + head) * D + (u % CH) * 8);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void store(const Pre& R, elem_t* stage) {
-    const int tid = threadIdx.x;
-    elem_t* Ks = stage;
-    elem_t* Vt = stage + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int u = tid + i * NT;
-      if (u < K_UNITS) *reinterpret_cast<u32x4_t*>(Ks + (u / CH) * KSTR + (u % CH) * 8) = R.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * NT;
-      if (u < V_UNITS) {
-        const int kap = (u / CH) * 4;          // first key of the group, within the tile
-        const int kc = kap >> 5, kl = kap & 31;
-        const int pos = kc * 32 + 8 * ((kl & 15) >> 2) + 4 * (kl >> 4);
-        const int d0 = (u % CH) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          unsigned lo, hi;
-          if (e & 1) {
-            lo = (R.v[i][0][w] >> 16) | (R.v[i][1][w] & 0xffff0000u);
-            hi = (R.v[i][2][w] >> 16) | (R.v[i][3][w] & 0xffff0000u);
-          } else {
-            lo = (R.v[i][0][w] & 0xffffu) | (R.v[i][1][w] << 16);
-            hi = (R.v[i][2][w] & 0xffffu) | (R.v[i][3][w] << 16);
-          }
-          *reinterpret_cast<u32x2_t*>(Vt + (d0 + e) * VSTR + pos) = u32x2_t{lo, hi};
-        }
-      }
-    }
-  }
-
-  // S^T[kb][qb] = K_tile . Q^T
-  static __device__ __forceinline__ void qk(f32x4_t (&S)[NKB][QB], const QOp& Q, const elem_t* stage, int lane) {
-    const int g = lane >> 4, c = lane & 15;
-    const elem_t* Ks = stage;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 16 + c) * KSTR + ks * 32 + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Q.x[qb][ks], S[kb][qb], 0, 0, 0);
-      }
-    }
-  }
-
-  // O^T[db][qb] += V^T_tile . P^T, P held in S (float32, already exponentiated)
-  static __device__ __forceinline__ void pv(f32x4_t (&O)[NDB][QB], const f32x4_t (&S)[NKB][QB],
-                                            const elem_t* stage, int lane) {
-    const int g = lane >> 4, c = lane & 15;
-    const elem_t* Vt = stage + K_ELEMS;
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      bf16x8_t pb[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pb[qb][j] = (__bf16)S[2 * kc][qb][j];
-          pb[qb][4 + j] = (__bf16)S[2 * kc + 1][qb][j];
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Vt + (db * 16 + c) * VSTR + kc * 32 + 8 * g);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          O[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qb], O[db][qb], 0, 0, 0);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void store_out(elem_t* __restrict__ o, size_t off, const f32x4_t& x, float inv) {
-    __bf16 t0 = (__bf16)(x[0] * inv), t1 = (__bf16)(x[1] * inv), t2 = (__bf16)(x[2] * inv), t3 = (__bf16)(x[3] * inv);
-    const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, t0) | ((unsigned)__builtin_bit_cast(unsigned short, t1) << 16);
-    const unsigned hi = (unsigned)__builtin_bit_cast(unsigned short, t2) | ((unsigned)__builtin_bit_cast(unsigned short, t3) << 16);
-    *reinterpret_cast<u32x2_t*>(o + off) = u32x2_t{lo, hi};
-  }
-};
-
 // float32 inputs: v_mfma_f32_16x16x4_f32 for both products (no bf16 rounding).
 template <int D_, int QB_, int NW_, int BN_>
 struct F32Traits {
@@ -480,7 +310,7 @@ struct F32Traits {
 // The attention kernel (persistent).
 // ----------------------------------------------------------------------------
 template <class T>
-__global__ __launch_bounds__(T::NT) void attn_fwd_kernel(
+__global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const typename T::elem_t* __restrict__ q, const typename T::elem_t* __restrict__ k,
     const typename T::elem_t* __restrict__ v, typename T::elem_t* __restrict__ o,
     const int32_t* __restrict__ cu, int n_seqs, int n_heads, float c2, int negate) {
@@ -613,6 +443,346 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: direct HBM->LDS staging, v_mfma_f32_16x16x32_bf16 for both products.
+//
+// LDS layout of one stage (one BN-key tile):
+//   K: [BN][KCH chunks of 16 B]  -- row stride KCH*4 words = 4*odd, so the 16-byte
+//      A-operand reads of 8 consecutive rows hit distinct banks.  Chunks past the
+//      head_dim hold a copy of real data (finite) and meet zero Q columns.
+//   V: [BN][VCH chunks of 16 B]  -- natural [key][d] order; read with the transposing
+//      ds_read_b64_tr_b16, whose 4-row x 32-byte footprint per 16 lanes is bank-conflict
+//      free with a row stride of 8 (mod 32) words.
+// Both are filled by global_load_lds_dwordx4: lane l of a wave-wide load lands at
+// base + 16*l, so each wave-wide load fills 64 consecutive chunk slots.
+// ---------------------------------------------------------------------------
+template <int D_, int QB_, int NW_, int BN_, bool SUM_MFMA_>
+struct Bf16Cfg {
+  using elem_t = __bf16;
+  static constexpr int D = D_, QB = QB_, NW = NW_, BN = BN_;
+  static constexpr bool SUM_MFMA = SUM_MFMA_;   // row sums by an MFMA against a block of ones
+  static constexpr int NT = NW * 64;
+  static constexpr int NQ = QB * 16;            // queries per wavefront
+  static constexpr int BM = NW * NQ;            // queries per work item
+  static constexpr int KSUB = 32;               // keys per compute step
+  static constexpr int NSUB = BN / KSUB;
+  static constexpr int NK32 = D / 32;           // Q.K^T contraction: 32-deep MFMA steps ...
+  static constexpr int TAIL = D % 32 ? 1 : 0;   // ... plus one 16-deep step (d past D zero)
+  static constexpr int DK = NK32 * 32 + 16 * TAIL;
+  static constexpr int DV = (D + 15) / 16 * 16; // O^T rows, padded
+  static constexpr int NDB = DV / 16;
+  static constexpr int NACC = NDB + (SUM_MFMA ? 1 : 0);
+  static constexpr int CH = D / 8;              // 16-byte chunks of a row in HBM
+  static constexpr int KCH = DK / 8 + 1;
+  static constexpr int VCH = D <= 80 ? 10 : 18;
+  static constexpr int KSTR = KCH * 8, VSTR = VCH * 8;  // elements
+  static constexpr int K_BYTES = BN * KCH * 16, V_BYTES = BN * VCH * 16;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int K_LOADS = BN * KCH / 64, V_LOADS = BN * VCH / 64;
+  static constexpr int LOADS = K_LOADS + V_LOADS;
+  static_assert(D % 8 == 0 && BN % 64 == 0 && D - NK32 * 32 <= 16, "tile shape");
+  static_assert(VCH * 8 >= DV && (VCH * 4) % 32 == 8, "V stride");
+  static_assert(((KCH * 4) / 4) % 2 == 1, "K stride");
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ float fbits(unsigned x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ unsigned ubits(float x) { return __builtin_bit_cast(unsigned, x); }
+
+// max over the four lanes l, l^16, l^32, l^48 (permlane swaps: VALU only, no LDS)
+__device__ __forceinline__ float max_4groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(ubits(x), ubits(x), false, false);
+  x = fmaxf(fbits(a[0]), fbits(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(ubits(x), ubits(x), false, false);
+  return fmaxf(fbits(b[0]), fbits(b[1]));
+}
+__device__ __forceinline__ float sum_4groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(ubits(x), ubits(x), false, false);
+  x = fbits(a[0]) + fbits(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(ubits(x), ubits(x), false, false);
+  return fbits(b[0]) + fbits(b[1]);
+}
+
+
+// Wave-wide DMA loads of one K/V tile.  Load i of wave w is the tile's load number
+// wl = w + i*NW; lane l of it fills chunk slot z = (wl or wl - K_LOADS)*64 + l of the
+// K or V area, i.e. key row z / per and chunk z % per (chunks past head_dim repeat
+// the last real chunk, so every byte copied is finite data of that row).
+template <class C>
+struct Dma {
+  static constexpr int PER_WAVE = (C::LOADS + C::NW - 1) / C::NW;
+
+  static __device__ __forceinline__ unsigned lane_offset(int wl, int lane, int key_limit, unsigned row_bytes) {
+    const bool is_k = wl < C::K_LOADS;
+    const int z = (is_k ? wl : wl - C::K_LOADS) * 64 + lane;
+    const int per = is_k ? C::KCH : C::VCH;
+    const int row = min(z / per, key_limit);
+    const int ch = min(z % per, C::CH - 1);
+    return (unsigned)row * row_bytes + (unsigned)ch * 16u;
+  }
+
+  // byte offsets (relative to the tile's first key row) for full tiles
+  static __device__ __forceinline__ void init(unsigned (&off)[PER_WAVE], int wave, int lane, unsigned row_bytes) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int wl = wave + i * C::NW;
+      off[i] = wl < C::LOADS ? lane_offset(wl, lane, C::BN - 1, row_bytes) : 0u;
+    }
+  }
+
+  // Enqueue the tile with keys [key0, key0 + BN); a RAGGED tile clamps rows to b - 1.
+  template <bool RAGGED>
+  static __device__ __forceinline__ void issue(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                               unsigned char* buf, int key0, int b, int head, int n_heads,
+                                               unsigned row_bytes, const unsigned (&off)[PER_WAVE], int wave,
+                                               int lane) {
+    const size_t base = ((size_t)key0 * n_heads + head) * C::D;
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(k + base);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(v + base);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int wl = wave + i * C::NW;
+      if (wl < C::LOADS) {
+        const bool is_k = wl < C::K_LOADS;
+        const unsigned o = RAGGED ? lane_offset(wl, lane, b - 1 - key0, row_bytes) : off[i];
+        const unsigned char* src = (is_k ? kb : vb) + o;
+        unsigned char* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+      }
+    }
+  }
+};
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// One compute step over 32 keys [kb0, kb0 + 32) of the LDS tile.  RAGGED: only the
+// first `kvalid` of them belong to the sequence.
+template <class C, bool RAGGED>
+__device__ __forceinline__ void attend_32(const __bf16* Ks, const __bf16* Vs, int kb0, int kvalid,
+                                         const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                         f32x4_t (&O)[C::NACC][C::QB],
+                                         float (&m)[C::QB], float (&lsum)[C::QB], float c2, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  // ---- S^T = K.Q^T: lane holds keys kb0+kb*16+4g+r of query c of each block qb
+  f32x4_t S[2][C::QB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) S[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < C::NK32; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb0 + kb * 16 + c) * C::KSTR + ks * 32 + 8 * g);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Q[qb][ks], S[kb][qb], 0, 0, 0);
+    }
+  if constexpr (C::TAIL) {  // dims NK32*32 + 4g..+4 in a 16-deep step
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const s16x4_t a = *reinterpret_cast<const s16x4_t*>(Ks + (kb0 + kb * 16 + c) * C::KSTR + C::NK32 * 32 + 4 * g);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, QT[qb], S[kb][qb], 0, 0, 0);
+    }
+  }
+  if constexpr (RAGGED) {  // keys past the sequence take no part in the max ...
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kb * 16 + 4 * g + r >= kvalid)
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) S[kb][qb][r] = -INFINITY;
+  }
+  // ---- row max over the 32 keys; the running max is raised only past kLazyTau
+  float alpha[C::QB];
+  bool raise = false;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float mx = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
+                     fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
+    mx = max_4groups(mx);
+    const float mc = mx * c2;
+    alpha[qb] = 1.f;
+    if (mc > m[qb] + kLazyTau) {
+      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mc);
+      m[qb] = mc;
+      raise = true;
+    }
+  }
+  if (__any(raise)) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      lsum[qb] *= alpha[qb];
+#pragma unroll
+      for (int db = 0; db < C::NACC; ++db) O[db][qb] *= alpha[qb];
+    }
+  }
+  // ---- P = exp2(S*c - m) as the bf16 B operand of O^T += V^T.P^T
+  bf16x8_t P[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float p[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[kb * 4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][r], c2, -m[qb]));
+    if constexpr (RAGGED) {  // ... and weigh exactly 0 (also when the scale is 0)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb * 16 + 4 * g + r >= kvalid) p[kb * 4 + r] = 0.f;
+    }
+    if constexpr (!C::SUM_MFMA) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lsum[qb] += p[j];
+    }
+    const u32x4_t w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                       cvt_pk_bf16(p[6], p[7])};
+    P[qb] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  // ---- V^T fragments: two transposing reads of [key][d] give lane (c, g) the keys
+  //      kb0+4g+0..3 and kb0+16+4g+0..3 of dim db*16+c, matching the P^T slots
+  const int i = lane & 15;
+  const __bf16* v1 = Vs + (kb0 + 4 * g + (i >> 2)) * C::VSTR + 4 * (i & 3);
+  const __bf16* v2 = v1 + 16 * C::VSTR;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v1 + db * 16));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v2 + db * 16));
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb], O[db][qb], 0, 0, 0);
+  }
+  if constexpr (C::SUM_MFMA) {  // row sums of the rounded weights, by MFMA against ones
+    const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+      O[C::NDB][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), P[qb],
+                                                               O[C::NDB][qb], 0, 0, 0);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, float c2, int negate) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
+  unsigned char* stage = smem + ((sizeof(PlanLds) + 15) / 16) * 16;
+
+  const int n_items = build_plan<C::NT>(plan, cu, n_seqs, n_heads, C::BM);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int G = gridDim.x;
+  const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const unsigned row_bytes = (unsigned)n_heads * C::D * 2u;
+  unsigned dma_off[Dma<C>::PER_WAVE];
+  Dma<C>::init(dma_off, wave, lane, row_bytes);
+
+  // Items in longest-first order are dealt out in rounds of G, alternating direction
+  // (round r, slot s -> item r*G + s, or r*G + G-1-s on odd rounds) to even out the load.
+  for (int round = 0;; ++round) {
+    const int it = round * G + ((round & 1) ? G - 1 - slot : slot);
+    if (it >= n_items) break;
+    const Item item = map_item(plan, n_seqs, it, C::BM);
+    const int qend = min(item.q0 + C::BM, item.b);
+    const int row0 = item.q0 + wave * C::NQ;
+    const int ntiles = ceil_div(item.b - item.a, C::BN);
+    const bool last_ragged = (item.b - item.a) % C::BN != 0;
+
+    __syncthreads();  // the previous item is done with both stage buffers
+    if (ntiles == 1 && last_ragged)
+      Dma<C>::template issue<true>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    else
+      Dma<C>::template issue<false>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+
+    // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
+    // 16-deep tail dims NK32*32+4g..+4 (zero past D)
+    bf16x8_t Q[C::QB][C::NK32];
+    s16x4_t QT[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int row = min(row0 + qb * 16 + c, qend - 1);
+      const __bf16* qrow = q + ((size_t)row * n_heads + item.head) * C::D;
+#pragma unroll
+      for (int ks = 0; ks < C::NK32; ++ks) {
+        u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
+        if (negate) w ^= 0x80008000u;
+        Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+      u32x2_t t = {0u, 0u};
+      if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
+      if (negate) t ^= 0x80008000u;
+      QT[qb] = __builtin_bit_cast(s16x4_t, t);
+    }
+
+    f32x4_t O[C::NACC][C::QB];
+#pragma unroll
+    for (int db = 0; db < C::NACC; ++db)
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[C::QB], lsum[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
+
+    for (int t = 0; t < ntiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+      __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+      const int key0 = item.a + t * C::BN;
+      if (t + 1 < ntiles) {
+        unsigned char* nb = stage + ((t + 1) & 1) * C::STAGE_BYTES;
+        if (t + 2 == ntiles && last_ragged)
+          Dma<C>::template issue<true>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off,
+                                       wave, lane);
+        else
+          Dma<C>::template issue<false>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off,
+                                        wave, lane);
+      }
+      const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
+      const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
+      const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub) {
+        const int kvalid = item.b - (key0 + sub * C::KSUB);
+        if (kvalid >= C::KSUB)
+          attend_32<C, false>(Ks, Vs, sub * C::KSUB, C::KSUB, Q, QT, O, m, lsum, c2, lane);
+        else if (kvalid > 0)
+          attend_32<C, true>(Ks, Vs, sub * C::KSUB, kvalid, Q, QT, O, m, lsum, c2, lane);
+      }
+    }
+
+    // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const float l = C::SUM_MFMA ? O[C::NDB][qb][0] : sum_4groups(lsum[qb]);
+      const float inv = 1.0f / l;
+      const int row = row0 + qb * 16 + c;
+      if (row < qend) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const int d0 = db * 16 + 4 * g;
+          if (d0 < C::D) {
+            const f32x4_t x = O[db][qb];
+            *reinterpret_cast<u32x2_t*>(o + ((size_t)row * n_heads + item.head) * C::D + d0) =
+                u32x2_t{cvt_pk_bf16(x[0] * inv, x[1] * inv), cvt_pk_bf16(x[2] * inv, x[3] * inv)};
+          }
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
@@ -633,9 +803,9 @@ struct KernelDesc {
 };
 
 template <class T>
-KernelDesc describe() {
+KernelDesc describe_f32() {
   KernelDesc d;
-  d.func = reinterpret_cast<const void*>(&attn_fwd_kernel<T>);
+  d.func = reinterpret_cast<const void*>(&attn_fwd_f32_kernel<T>);
   d.bm = T::BM;
   d.bn = T::BN;
   d.waves = T::NW;
@@ -644,11 +814,35 @@ KernelDesc describe() {
   return d;
 }
 
+template <class C>
+KernelDesc describe_bf16() {
+  KernelDesc d;
+  d.func = reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C>);
+  d.bm = C::BM;
+  d.bn = C::BN;
+  d.waves = C::NW;
+  d.nt = C::NT;
+  d.lds = ((sizeof(PlanLds) + 15) / 16) * 16 + 2 * (size_t)C::STAGE_BYTES;
+  return d;
+}
+
 // Tile choices per (dtype, head_dim).
-using K_bf16_64 = Bf16Traits<64, 2, 4, 64>;
-using K_bf16_72 = Bf16Traits<72, 2, 4, 64>;
-using K_bf16_80 = Bf16Traits<80, 2, 4, 64>;
-using K_bf16_128 = Bf16Traits<128, 2, 4, 64>;
+#ifndef VITATTN_BF16_QB
+#define VITATTN_BF16_QB 4
+#endif
+#ifndef VITATTN_BF16_NW
+#define VITATTN_BF16_NW 4
+#endif
+#ifndef VITATTN_BF16_QB_128
+#define VITATTN_BF16_QB_128 2
+#endif
+#ifndef VITATTN_BF16_SUM_MFMA
+#define VITATTN_BF16_SUM_MFMA true
+#endif
+using K_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using K_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using K_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using K_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_128, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
 using K_f32_64 = F32Traits<64, 1, 4, 32>;
 using K_f32_72 = F32Traits<72, 1, 4, 32>;
 using K_f32_80 = F32Traits<80, 1, 4, 32>;
@@ -668,14 +862,14 @@ int kernel_index(int32_t head_dim, int32_t dtype) {
 
 KernelDesc kernel_desc(int idx) {
   switch (idx) {
-    case 0: return describe<K_f32_64>();
-    case 1: return describe<K_f32_72>();
-    case 2: return describe<K_f32_80>();
-    case 3: return describe<K_f32_128>();
-    case 4: return describe<K_bf16_64>();
-    case 5: return describe<K_bf16_72>();
-    case 6: return describe<K_bf16_80>();
-    default: return describe<K_bf16_128>();
+    case 0: return describe_f32<K_f32_64>();
+    case 1: return describe_f32<K_f32_72>();
+    case 2: return describe_f32<K_f32_80>();
+    case 3: return describe_f32<K_f32_128>();
+    case 4: return describe_bf16<K_bf16_64>();
+    case 5: return describe_bf16<K_bf16_72>();
+    case 6: return describe_bf16<K_bf16_80>();
+    default: return describe_bf16<K_bf16_128>();
   }
 }
 

@@ -96,13 +96,21 @@ def cpu_baseline(name: str, target_s: float = 12.0):
 
 
 def load_traffic(name: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if present and current."""
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
+    when there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+
     path = os.path.join(PROFILES, f"attn_fwd_bf16_d80_{name}_hbm_traffic.json")
+    src = os.path.join(ROOT, "vision_transformer_attention_amd", "csrc", "vitattn.hip")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
         return rec.get("bytes_per_launch")
     except Exception:
         return None

@@ -674,112 +674,139 @@ __device__ __forceinline__ void attend_32(const __bf16* Ks, const __bf16* Vs, in
   }
 }
 
+// One work item (sequence, head, BM queries from q0) for the whole workgroup.  The K/V
+// stage buffers and the DMA offsets depend only on head_dim and the tile shape, so work
+// items of different query-block sizes (C::QB) share them.
 template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
+__device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                         const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads, float c2,
+                                         int negate, unsigned char* stage, unsigned row_bytes,
+                                         const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int qend = min(item.q0 + C::BM, item.b);
+  const int row0 = item.q0 + wave * C::NQ;
+  const int ntiles = ceil_div(item.b - item.a, C::BN);
+  const bool last_ragged = (item.b - item.a) % C::BN != 0;
+
+  __syncthreads();  // the previous item is done with both stage buffers
+  if (ntiles == 1 && last_ragged)
+    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+  else
+    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+
+  // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
+  // 16-deep tail dims NK32*32+4g..+4 (zero past D)
+  bf16x8_t Q[C::QB][C::NK32];
+  s16x4_t QT[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int row = min(row0 + qb * 16 + c, qend - 1);
+    const __bf16* qrow = q + ((size_t)row * n_heads + item.head) * C::D;
+#pragma unroll
+    for (int ks = 0; ks < C::NK32; ++ks) {
+      u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
+      if (negate) w ^= 0x80008000u;
+      Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    u32x2_t t = {0u, 0u};
+    if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
+    if (negate) t ^= 0x80008000u;
+    QT[qb] = __builtin_bit_cast(s16x4_t, t);
+  }
+
+  f32x4_t O[C::NACC][C::QB];
+#pragma unroll
+  for (int db = 0; db < C::NACC; ++db)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[C::QB], lsum[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
+
+  for (int t = 0; t < ntiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+    __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+    const int key0 = item.a + t * C::BN;
+    if (t + 1 < ntiles) {
+      unsigned char* nb = stage + ((t + 1) & 1) * C::STAGE_BYTES;
+      if (t + 2 == ntiles && last_ragged)
+        Dma<C>::template issue<true>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off, wave,
+                                     lane);
+      else
+        Dma<C>::template issue<false>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off, wave,
+                                      lane);
+    }
+    const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
+    const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
+    const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const int kvalid = item.b - (key0 + sub * C::KSUB);
+      if (kvalid >= C::KSUB)
+        attend_32<C, false>(Ks, Vs, sub * C::KSUB, C::KSUB, Q, QT, O, m, lsum, c2, lane);
+      else if (kvalid > 0)
+        attend_32<C, true>(Ks, Vs, sub * C::KSUB, kvalid, Q, QT, O, m, lsum, c2, lane);
+    }
+  }
+
+  // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const float l = C::SUM_MFMA ? O[C::NDB][qb][0] : sum_4groups(lsum[qb]);
+    const float inv = 1.0f / l;
+    const int row = row0 + qb * 16 + c;
+    if (row < qend) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d0 = db * 16 + 4 * g;
+        if (d0 < C::D) {
+          const f32x4_t x = O[db][qb];
+          *reinterpret_cast<u32x2_t*>(o + ((size_t)row * n_heads + item.head) * C::D + d0) =
+              u32x2_t{cvt_pk_bf16(x[0] * inv, x[1] * inv), cvt_pk_bf16(x[2] * inv, x[3] * inv)};
+        }
+      }
+    }
+  }
+}
+
+// The bf16 kernel.  CA and CB differ only in the queries per wavefront (CA::QB > CB::QB).
+// The launch works with CA's large query blocks unless they would leave most of the grid
+// idle (a short single image), in which case it re-plans with CB's small blocks: more
+// items, so more of the machine works, each item over the same keys.
+template <class CA, class CB>
+__global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, float c2, int negate) {
+  static_assert(CA::D == CB::D && CA::NW == CB::NW && CA::BN == CB::BN && CA::STAGE_BYTES == CB::STAGE_BYTES,
+                "the two query-block sizes share the staging layout");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
   unsigned char* stage = smem + ((sizeof(PlanLds) + 15) / 16) * 16;
 
-  const int n_items = build_plan<C::NT>(plan, cu, n_seqs, n_heads, C::BM);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int G = gridDim.x;
+  int n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CA::BM);
+  const bool small = 2 * n_items < G;  // the same decision in every workgroup
+  if (small) {
+    __syncthreads();  // everyone has read the first plan's item count
+    n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CB::BM);
+  }
+  const int bm = small ? CB::BM : CA::BM;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const unsigned row_bytes = (unsigned)n_heads * C::D * 2u;
-  unsigned dma_off[Dma<C>::PER_WAVE];
-  Dma<C>::init(dma_off, wave, lane, row_bytes);
+  const unsigned row_bytes = (unsigned)n_heads * CA::D * 2u;
+  unsigned dma_off[Dma<CA>::PER_WAVE];
+  Dma<CA>::init(dma_off, wave, lane, row_bytes);
 
   // Items in longest-first order are dealt out in rounds of G, alternating direction
   // (round r, slot s -> item r*G + s, or r*G + G-1-s on odd rounds) to even out the load.
   for (int round = 0;; ++round) {
     const int it = round * G + ((round & 1) ? G - 1 - slot : slot);
     if (it >= n_items) break;
-    const Item item = map_item(plan, n_seqs, it, C::BM);
-    const int qend = min(item.q0 + C::BM, item.b);
-    const int row0 = item.q0 + wave * C::NQ;
-    const int ntiles = ceil_div(item.b - item.a, C::BN);
-    const bool last_ragged = (item.b - item.a) % C::BN != 0;
-
-    __syncthreads();  // the previous item is done with both stage buffers
-    if (ntiles == 1 && last_ragged)
-      Dma<C>::template issue<true>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    const Item item = map_item(plan, n_seqs, it, bm);
+    if (small)
+      run_item<CB>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);
     else
-      Dma<C>::template issue<false>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
-
-    // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
-    // 16-deep tail dims NK32*32+4g..+4 (zero past D)
-    bf16x8_t Q[C::QB][C::NK32];
-    s16x4_t QT[C::QB];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int row = min(row0 + qb * 16 + c, qend - 1);
-      const __bf16* qrow = q + ((size_t)row * n_heads + item.head) * C::D;
-#pragma unroll
-      for (int ks = 0; ks < C::NK32; ++ks) {
-        u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
-        if (negate) w ^= 0x80008000u;
-        Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
-      }
-      u32x2_t t = {0u, 0u};
-      if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
-      if (negate) t ^= 0x80008000u;
-      QT[qb] = __builtin_bit_cast(s16x4_t, t);
-    }
-
-    f32x4_t O[C::NACC][C::QB];
-#pragma unroll
-    for (int db = 0; db < C::NACC; ++db)
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[C::QB], lsum[C::QB];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
-
-    for (int t = 0; t < ntiles; ++t) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
-      __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
-      const int key0 = item.a + t * C::BN;
-      if (t + 1 < ntiles) {
-        unsigned char* nb = stage + ((t + 1) & 1) * C::STAGE_BYTES;
-        if (t + 2 == ntiles && last_ragged)
-          Dma<C>::template issue<true>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off,
-                                       wave, lane);
-        else
-          Dma<C>::template issue<false>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off,
-                                        wave, lane);
-      }
-      const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
-      const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
-      const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub) {
-        const int kvalid = item.b - (key0 + sub * C::KSUB);
-        if (kvalid >= C::KSUB)
-          attend_32<C, false>(Ks, Vs, sub * C::KSUB, C::KSUB, Q, QT, O, m, lsum, c2, lane);
-        else if (kvalid > 0)
-          attend_32<C, true>(Ks, Vs, sub * C::KSUB, kvalid, Q, QT, O, m, lsum, c2, lane);
-      }
-    }
-
-    // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const float l = C::SUM_MFMA ? O[C::NDB][qb][0] : sum_4groups(lsum[qb]);
-      const float inv = 1.0f / l;
-      const int row = row0 + qb * 16 + c;
-      if (row < qend) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const int d0 = db * 16 + 4 * g;
-          if (d0 < C::D) {
-            const f32x4_t x = O[db][qb];
-            *reinterpret_cast<u32x2_t*>(o + ((size_t)row * n_heads + item.head) * C::D + d0) =
-                u32x2_t{cvt_pk_bf16(x[0] * inv, x[1] * inv), cvt_pk_bf16(x[2] * inv, x[3] * inv)};
-          }
-        }
-      }
-    }
+      run_item<CA>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);
   }
 }
 
@@ -814,10 +841,10 @@ KernelDesc describe_f32() {
   return d;
 }
 
-template <class C>
+template <class C, class CB>
 KernelDesc describe_bf16() {
   KernelDesc d;
-  d.func = reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C>);
+  d.func = reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C, CB>);
   d.bm = C::BM;
   d.bn = C::BN;
   d.waves = C::NW;
@@ -839,10 +866,17 @@ KernelDesc describe_bf16() {
 #ifndef VITATTN_BF16_SUM_MFMA
 #define VITATTN_BF16_SUM_MFMA true
 #endif
+#ifndef VITATTN_BF16_QB_SMALL
+#define VITATTN_BF16_QB_SMALL 1
+#endif
 using K_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
 using K_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
 using K_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
 using K_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_128, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using S_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using S_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using S_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using S_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
 using K_f32_64 = F32Traits<64, 1, 4, 32>;
 using K_f32_72 = F32Traits<72, 1, 4, 32>;
 using K_f32_80 = F32Traits<80, 1, 4, 32>;
@@ -866,10 +900,10 @@ KernelDesc kernel_desc(int idx) {
     case 1: return describe_f32<K_f32_72>();
     case 2: return describe_f32<K_f32_80>();
     case 3: return describe_f32<K_f32_128>();
-    case 4: return describe_bf16<K_bf16_64>();
-    case 5: return describe_bf16<K_bf16_72>();
-    case 6: return describe_bf16<K_bf16_80>();
-    default: return describe_bf16<K_bf16_128>();
+    case 4: return describe_bf16<K_bf16_64, S_bf16_64>();
+    case 5: return describe_bf16<K_bf16_72, S_bf16_72>();
+    case 6: return describe_bf16<K_bf16_80, S_bf16_80>();
+    default: return describe_bf16<K_bf16_128, S_bf16_128>();
   }
 }
 

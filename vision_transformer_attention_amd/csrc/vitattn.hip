@@ -25,26 +25,27 @@
 //    query tile)), then walks the item list with a stride of the grid size.
 //    Slots are assigned so that the workgroups of one XCD (blockIdx % 8) take
 //    consecutive items, which share a (sequence, head) and so its K/V in that
-//    XCD's L2.
+//    XCD's L2.  When the large query tiles would leave most of the grid idle (one
+//    short image), the launch re-plans with small ones.
 //  * Scores are computed transposed, S^T = K.Q^T, with v_mfma_f32_16x16x32_bf16
 //    (float32: v_mfma_f32_16x16x4_f32).  In that accumulator layout a lane holds
-//    4 keys of one query, so the row max is in-lane plus two cross-lane steps,
-//    and the same registers (converted to bf16) are directly the B operand of
+//    4 keys of one query, so a row max is in-lane plus two cross-lane steps, and
+//    the same registers (converted to bf16) are directly the B operand of
 //    O^T += V^T.P^T: no data movement between the two products, and the running
-//    output of a query sits in the lane that owns its softmax state, so the
-//    rescale is a per-lane multiply.
-//  * The running max is raised lazily: only when a tile's max exceeds it by more
-//    than kLazyTau (log2 units).  Exponentials are then at most 2^kLazyTau, which
-//    float32 sums and bf16 weights carry without loss, and the accumulator rescale
-//    is skipped (wave-uniform branch) on almost every tile.  The final division by
-//    the row sum makes the result independent of which max was used.
-//  * K tiles sit in LDS as [key][d] and V tiles as V^T [d][key] (transposed while
-//    staging, with the keys permuted to match the P^T register layout), both with
-//    16-byte row padding against bank conflicts and double-buffered: tile t+1 is
-//    fetched into registers while tile t is computed.
-//  * head_dim 72 and 80 are zero-padded to 96 for the Q.K^T contraction (K steps of
-//    32) and to 80 for the P.V output rows (blocks of 16); padded K columns are
-//    zeroed in LDS once, padded Q columns are zero in registers.
+//    output of a query sits in the lane that owns its softmax state, so a rescale
+//    is a per-lane multiply.
+//  * bf16: K/V tiles go HBM -> LDS by global_load_lds_dwordx4 (no VGPRs, no LDS
+//    write instructions), double-buffered, K as [key][d] and V as [key][d] read
+//    transposed by ds_read_b64_tr_b16, rows padded against bank conflicts.  The
+//    exponent offset of each query row is fixed by the first 32 keys and kept
+//    while no weight reaches 2 (an in-lane max decides, no cross-lane reduction);
+//    the rare rise past that is handled by a rescale.  Row sums come from one more
+//    MFMA against a block of ones.  The last tile of a sequence ends at its last
+//    key, so only the first step of a work item is partial.
+//  * float32: K/V staged through registers (V transposed while staging), running
+//    max raised lazily (only past kLazyTau) with a wave-uniform rescale.
+//  * head_dim 72 and 80 use a 16-deep tail step in Q.K^T (dims past D are zero in
+//    Q) and are padded to 80 for the P.V output rows (blocks of 16).
 #include "vitattn.h"
 
 #include <hip/hip_runtime.h>
@@ -64,7 +65,8 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxSeqs = 512;     // sequences planned by one launch (more: several launches)
 constexpr int kSortMax = 256;     // sequences ordered longest-first up to this count
-constexpr float kLazyTau = 8.0f;  // headroom (log2) before the running max is raised
+constexpr float kLazyTau = 8.0f;  // float32 kernel: headroom (log2) before the running max is raised
+constexpr float kHeadroom = 16.0f;  // bf16 kernel: log2 gap between the reference max and the exponent offset
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------------------
@@ -456,11 +458,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 // Both are filled by global_load_lds_dwordx4: lane l of a wave-wide load lands at
 // base + 16*l, so each wave-wide load fills 64 consecutive chunk slots.
 // ---------------------------------------------------------------------------
-template <int D_, int QB_, int NW_, int BN_, bool SUM_MFMA_>
+template <int D_, int QB_, int NW_, int BN_>
 struct Bf16Cfg {
   using elem_t = __bf16;
   static constexpr int D = D_, QB = QB_, NW = NW_, BN = BN_;
-  static constexpr bool SUM_MFMA = SUM_MFMA_;   // row sums by an MFMA against a block of ones
   static constexpr int NT = NW * 64;
   static constexpr int NQ = QB * 16;            // queries per wavefront
   static constexpr int BM = NW * NQ;            // queries per work item
@@ -471,7 +472,7 @@ struct Bf16Cfg {
   static constexpr int DK = NK32 * 32 + 16 * TAIL;
   static constexpr int DV = (D + 15) / 16 * 16; // O^T rows, padded
   static constexpr int NDB = DV / 16;
-  static constexpr int NACC = NDB + (SUM_MFMA ? 1 : 0);
+  static constexpr int NACC = NDB + 1;         // plus one block for the row sums
   static constexpr int CH = D / 8;              // 16-byte chunks of a row in HBM
   static constexpr int KCH = DK / 8 + 1;
   static constexpr int VCH = D <= 80 ? 10 : 18;
@@ -499,12 +500,6 @@ __device__ __forceinline__ float max_4groups(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(ubits(x), ubits(x), false, false);
   return fmaxf(fbits(b[0]), fbits(b[1]));
 }
-__device__ __forceinline__ float sum_4groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(ubits(x), ubits(x), false, false);
-  x = fbits(a[0]) + fbits(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(ubits(x), ubits(x), false, false);
-  return fbits(b[0]) + fbits(b[1]);
-}
 
 
 // Wave-wide DMA loads of one K/V tile.  Load i of wave w is the tile's load number
@@ -515,11 +510,13 @@ template <class C>
 struct Dma {
   static constexpr int PER_WAVE = (C::LOADS + C::NW - 1) / C::NW;
 
-  static __device__ __forceinline__ unsigned lane_offset(int wl, int lane, int key_limit, unsigned row_bytes) {
+  // Byte offset of lane `lane` of load `wl` relative to the tile's row `lead`; rows of the
+  // tile before `lead` are filled with copies of row `lead`.
+  static __device__ __forceinline__ unsigned lane_offset(int wl, int lane, int lead, unsigned row_bytes) {
     const bool is_k = wl < C::K_LOADS;
     const int z = (is_k ? wl : wl - C::K_LOADS) * 64 + lane;
     const int per = is_k ? C::KCH : C::VCH;
-    const int row = min(z / per, key_limit);
+    const int row = max(z / per, lead) - lead;
     const int ch = min(z % per, C::CH - 1);
     return (unsigned)row * row_bytes + (unsigned)ch * 16u;
   }
@@ -529,14 +526,15 @@ struct Dma {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int wl = wave + i * C::NW;
-      off[i] = wl < C::LOADS ? lane_offset(wl, lane, C::BN - 1, row_bytes) : 0u;
+      off[i] = wl < C::LOADS ? lane_offset(wl, lane, 0, row_bytes) : 0u;
     }
   }
 
-  // Enqueue the tile with keys [key0, key0 + BN); a RAGGED tile clamps rows to b - 1.
-  template <bool RAGGED>
+  // Enqueue the tile whose rows are keys [key0 - lead, key0 - lead + BN): rows before key0
+  // (LEAD, the first tile of a sequence whose length is not a multiple of BN) repeat key0.
+  template <bool LEAD>
   static __device__ __forceinline__ void issue(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-                                               unsigned char* buf, int key0, int b, int head, int n_heads,
+                                               unsigned char* buf, int key0, int lead, int head, int n_heads,
                                                unsigned row_bytes, const unsigned (&off)[PER_WAVE], int wave,
                                                int lane) {
     const size_t base = ((size_t)key0 * n_heads + head) * C::D;
@@ -547,7 +545,7 @@ struct Dma {
       const int wl = wave + i * C::NW;
       if (wl < C::LOADS) {
         const bool is_k = wl < C::K_LOADS;
-        const unsigned o = RAGGED ? lane_offset(wl, lane, b - 1 - key0, row_bytes) : off[i];
+        const unsigned o = LEAD ? lane_offset(wl, lane, lead, row_bytes) : off[i];
         const unsigned char* src = (is_k ? kb : vb) + o;
         unsigned char* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
@@ -563,16 +561,50 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// One compute step over 32 keys [kb0, kb0 + 32) of the LDS tile.  RAGGED: only the
-// first `kvalid` of them belong to the sequence.
-template <class C, bool RAGGED>
-__device__ __forceinline__ void attend_32(const __bf16* Ks, const __bf16* Vs, int kb0, int kvalid,
-                                         const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
-                                         f32x4_t (&O)[C::NACC][C::QB],
-                                         float (&m)[C::QB], float (&lsum)[C::QB], float c2, int lane) {
+// Operand fragments of one 32-key compute step, read from the LDS tile.
+//   K (A operand of S^T = K.Q^T): lane (c, g) holds key kb0+kb*16+c, dims ks*32+8g..+8,
+//     and for the 16-deep tail dims NK32*32+4g..+4.
+//   V^T (A operand of O^T += V^T.P^T): two transposing reads of [key][d] give lane (c, g)
+//     keys kb0+4g+0..3 and kb0+16+4g+0..3 of dim db*16+c, matching the P^T slots.
+template <class C>
+struct KFrag {
+  bf16x8_t a[2][C::NK32];
+  s16x4_t t[2];
+};
+template <class C>
+struct VFrag {
+  bf16x8_t a[C::NDB];
+};
+
+template <class C>
+__device__ __forceinline__ void load_k(KFrag<C>& f, const __bf16* Ks, int kb0, int lane) {
   const int g = lane >> 4, c = lane & 15;
-  // ---- S^T = K.Q^T: lane holds keys kb0+kb*16+4g+r of query c of each block qb
-  f32x4_t S[2][C::QB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const __bf16* row = Ks + (kb0 + kb * 16 + c) * C::KSTR;
+#pragma unroll
+    for (int ks = 0; ks < C::NK32; ++ks) f.a[kb][ks] = *reinterpret_cast<const bf16x8_t*>(row + ks * 32 + 8 * g);
+    if constexpr (C::TAIL) f.t[kb] = *reinterpret_cast<const s16x4_t*>(row + C::NK32 * 32 + 4 * g);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void load_v(VFrag<C>& f, const __bf16* Vs, int kb0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const __bf16* v1 = Vs + (kb0 + 4 * g + (i >> 2)) * C::VSTR + 4 * (i & 3);
+  const __bf16* v2 = v1 + 16 * C::VSTR;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v1 + db * 16));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v2 + db * 16));
+    f.a[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+// S^T = K.Q^T for 32 keys: S[kb][qb][r] is key kb0+kb*16+4g+r of query row0+qb*16+c.
+template <class C>
+__device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K, const bf16x8_t (&Q)[C::QB][C::NK32],
+                                      const s16x4_t (&QT)[C::QB]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -580,103 +612,140 @@ __device__ __forceinline__ void attend_32(const __bf16* Ks, const __bf16* Vs, in
 #pragma unroll
   for (int ks = 0; ks < C::NK32; ++ks)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb0 + kb * 16 + c) * C::KSTR + ks * 32 + 8 * g);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
-        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Q[qb][ks], S[kb][qb], 0, 0, 0);
-    }
-  if constexpr (C::TAIL) {  // dims NK32*32 + 4g..+4 in a 16-deep step
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K.a[kb][ks], Q[qb][ks], S[kb][qb], 0, 0, 0);
+  if constexpr (C::TAIL) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const s16x4_t a = *reinterpret_cast<const s16x4_t*>(Ks + (kb0 + kb * 16 + c) * C::KSTR + C::NK32 * 32 + 4 * g);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
-        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, QT[qb], S[kb][qb], 0, 0, 0);
-    }
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(K.t[kb], QT[qb], S[kb][qb], 0, 0, 0);
   }
-  if constexpr (RAGGED) {  // keys past the sequence take no part in the max ...
+}
+
+// Softmax weights and O^T += V^T.P^T for one 32-key step.
+//
+// The exponent offset of query row i is M_i = (reference max of c2*s over the keys seen)
+// + kHeadroom, and the weights are p = exp2(c2*s - M_i), so the largest weight at the
+// time M_i was set is 2^-kHeadroom.  FIRST (the first step of a work item) sets M from
+// this step's exact row maxima.  Later steps keep M while every offset c2*s - M stays
+// below 1 (weights below 2), which one in-lane max decides for the whole wavefront
+// without any cross-lane reduction; otherwise (a row max rose by more than kHeadroom + 1)
+// the rows concerned move M up to their new maximum and rescale their running output
+// and sum before the weights are taken.  The final division by the row sum removes M from the
+// result, so the choice of M only has to keep the weights in range.
+//
+// Only the FIRST step of an item can hold keys outside the sequence: its first `kinv`
+// keys, which take no part in the max and get weight exactly 0 (also when c2 is 0).
+template <class C, bool FIRST>
+__device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
+                                              f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
+                                              int lane) {
+  const int g = lane >> 4;
+  if constexpr (FIRST) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (kb * 16 + 4 * g + r >= kvalid)
+        if (kb * 16 + 4 * g + r < kinv)
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb) S[kb][qb][r] = -INFINITY;
-  }
-  // ---- row max over the 32 keys; the running max is raised only past kLazyTau
-  float alpha[C::QB];
-  bool raise = false;
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    float mx = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
-                     fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
-    mx = max_4groups(mx);
-    const float mc = mx * c2;
-    alpha[qb] = 1.f;
-    if (mc > m[qb] + kLazyTau) {
-      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mc);
-      m[qb] = mc;
-      raise = true;
-    }
-  }
-  if (__any(raise)) {
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
-      lsum[qb] *= alpha[qb];
-#pragma unroll
-      for (int db = 0; db < C::NACC; ++db) O[db][qb] *= alpha[qb];
+      float mx = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
+                       fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
+      mx = max_4groups(mx);  // finite: at least one key of the step is in the sequence
+      negM[qb] = -__builtin_fmaf(mx, c2, kHeadroom);
     }
   }
-  // ---- P = exp2(S*c - m) as the bf16 B operand of O^T += V^T.P^T
-  bf16x8_t P[C::QB];
+  // t = c2*s - M, in place
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    float p[8];
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float t = __builtin_fmaf(S[kb][qb][r], c2, negM[qb]);
+        if constexpr (FIRST) t = (kb * 16 + 4 * g + r >= kinv) ? t : -INFINITY;
+        S[kb][qb][r] = t;
+      }
+  if constexpr (!FIRST) {
+    // one in-lane max over all of the lane's offsets decides for the whole wavefront
+    float hi = S[0][0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[kb * 4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][r], c2, -m[qb]));
-    if constexpr (RAGGED) {  // ... and weigh exactly 0 (also when the scale is 0)
+      for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 4; ++r) hi = fmaxf(hi, S[kb][qb][r]);
+    if (__builtin_expect(__any(hi >= 1.0f), 0)) {  // rare: some row max rose by more than kHeadroom + 1
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb * 16 + 4 * g + r >= kvalid) p[kb * 4 + r] = 0.f;
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float tm = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
+                         fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
+        tm = max_4groups(tm);
+        if (tm >= 1.0f) {  // the same decision in all four lanes of the row
+          const float delta = tm + kHeadroom;
+          negM[qb] -= delta;
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+          for (int db = 0; db < C::NACC; ++db) O[db][qb] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[kb][qb][r] -= delta;
+        }
+      }
     }
-    if constexpr (!C::SUM_MFMA) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lsum[qb] += p[j];
-    }
-    const u32x4_t w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
-                       cvt_pk_bf16(p[6], p[7])};
-    P[qb] = __builtin_bit_cast(bf16x8_t, w);
   }
-  // ---- V^T fragments: two transposing reads of [key][d] give lane (c, g) the keys
-  //      kb0+4g+0..3 and kb0+16+4g+0..3 of dim db*16+c, matching the P^T slots
-  const int i = lane & 15;
-  const __bf16* v1 = Vs + (kb0 + 4 * g + (i >> 2)) * C::VSTR + 4 * (i & 3);
-  const __bf16* v2 = v1 + 16 * C::VSTR;
+  // The V^T reads are issued only now, after every score MFMA of the step has been
+  // consumed: an LDS read may then reuse those MFMAs' operand registers safely, and its
+  // latency still hides behind the exponentials.
+  VFrag<C> V;
+  load_v<C>(V, Vs, kb0, lane);
+  u32x4_t W[C::QB];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v1 + db * 16));
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(v2 + db * 16));
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb], O[db][qb], 0, 0, 0);
-  }
-  if constexpr (C::SUM_MFMA) {  // row sums of the rounded weights, by MFMA against ones
-    const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    for (int j = 0; j < 4; ++j)
+      W[qb][j] = cvt_pk_bf16(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
+                             __builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2 + 1]));
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
-      O[C::NDB][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones), P[qb],
-                                                               O[C::NDB][qb], 0, 0, 0);
+      O[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb], 0, 0, 0);
+  // row sums of the rounded weights, by an MFMA against a block of ones
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+    O[C::NDB][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones),
+                                                             __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb], 0, 0, 0);
+}
+
+// One 32-key step [kb0, kb0 + 32) of the LDS tile: operand reads, both products, softmax.
+template <class C, bool FIRST>
+__device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int kb0, int kinv,
+                                        const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                        f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int lane) {
+  f32x4_t S[2][C::QB];
+  {
+    KFrag<C> kf;
+    load_k<C>(kf, Ks, kb0, lane);
+    qk_32<C>(S, kf, Q, QT);
   }
+  softmax_pv_32<C, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
 }
 
 // One work item (sequence, head, BM queries from q0) for the whole workgroup.  The K/V
 // stage buffers and the DMA offsets depend only on head_dim and the tile shape, so work
 // items of different query-block sizes (C::QB) share them.
+//
+// The keys [a, b) are covered by ntiles tiles of BN keys that END at b: tile 0 starts
+// `pad` = ntiles*BN - (b - a) keys before a, its first pad rows repeat key a in LDS and
+// are masked in the first step, and every later step is a full one.
 template <class C>
 __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads, float c2,
@@ -686,13 +755,14 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   const int qend = min(item.q0 + C::BM, item.b);
   const int row0 = item.q0 + wave * C::NQ;
   const int ntiles = ceil_div(item.b - item.a, C::BN);
-  const bool last_ragged = (item.b - item.a) % C::BN != 0;
+  const int pad = ntiles * C::BN - (item.b - item.a);  // 0 <= pad < BN
+  const int kstart = item.a - pad;                      // key of tile 0's row 0 (may precede a)
 
   __syncthreads();  // the previous item is done with both stage buffers
-  if (ntiles == 1 && last_ragged)
-    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+  if (pad > 0)
+    Dma<C>::template issue<true>(k, v, stage, item.a, pad, item.head, n_heads, row_bytes, dma_off, wave, lane);
   else
-    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<false>(k, v, stage, item.a, 0, item.head, n_heads, row_bytes, dma_off, wave, lane);
 
   // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
   // 16-deep tail dims NK32*32+4g..+4 (zero past D)
@@ -719,41 +789,40 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   for (int db = 0; db < C::NACC; ++db)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[C::QB], lsum[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
+  float negM[C::QB];
 
-  for (int t = 0; t < ntiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
-    __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
-    const int key0 = item.a + t * C::BN;
-    if (t + 1 < ntiles) {
-      unsigned char* nb = stage + ((t + 1) & 1) * C::STAGE_BYTES;
-      if (t + 2 == ntiles && last_ragged)
-        Dma<C>::template issue<true>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off, wave,
-                                     lane);
-      else
-        Dma<C>::template issue<false>(k, v, nb, key0 + C::BN, item.b, item.head, n_heads, row_bytes, dma_off, wave,
-                                      lane);
+  // tile 0: the first step with a key in the sequence sets the exponent offsets
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile 0 has landed
+  __syncthreads();                                   // every wave's has
+  if (ntiles > 1)
+    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, 0, item.head, n_heads, row_bytes,
+                                  dma_off, wave, lane);
+  const int s0 = pad / C::KSUB;
+  {
+    const __bf16* Ks = reinterpret_cast<const __bf16*>(stage);
+    const __bf16* Vs = reinterpret_cast<const __bf16*>(stage + C::K_BYTES);
+    step_32<C, true>(Ks, Vs, s0 * C::KSUB, pad - s0 * C::KSUB, Q, QT, O, negM, c2, lane);
+  }
+  // every later step: full, in order; a new tile starts at each multiple of NSUB
+  const int nsteps = ntiles * C::NSUB;
+  for (int st = s0 + 1; st < nsteps; ++st) {
+    const int t = st / C::NSUB, sub = st % C::NSUB;
+    if (sub == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+      __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+      if (t + 1 < ntiles)
+        Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, 0,
+                                      item.head, n_heads, row_bytes, dma_off, wave, lane);
     }
     const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
-    const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
-    const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int kvalid = item.b - (key0 + sub * C::KSUB);
-      if (kvalid >= C::KSUB)
-        attend_32<C, false>(Ks, Vs, sub * C::KSUB, C::KSUB, Q, QT, O, m, lsum, c2, lane);
-      else if (kvalid > 0)
-        attend_32<C, true>(Ks, Vs, sub * C::KSUB, kvalid, Q, QT, O, m, lsum, c2, lane);
-    }
+    step_32<C, false>(reinterpret_cast<const __bf16*>(buf), reinterpret_cast<const __bf16*>(buf + C::K_BYTES),
+                      sub * C::KSUB, 0, Q, QT, O, negM, c2, lane);
   }
 
   // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    const float l = C::SUM_MFMA ? O[C::NDB][qb][0] : sum_4groups(lsum[qb]);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / O[C::NDB][qb][0];
     const int row = row0 + qb * 16 + c;
     if (row < qend) {
 #pragma unroll
@@ -863,20 +932,17 @@ KernelDesc describe_bf16() {
 #ifndef VITATTN_BF16_QB_128
 #define VITATTN_BF16_QB_128 2
 #endif
-#ifndef VITATTN_BF16_SUM_MFMA
-#define VITATTN_BF16_SUM_MFMA true
-#endif
 #ifndef VITATTN_BF16_QB_SMALL
 #define VITATTN_BF16_QB_SMALL 1
 #endif
-using K_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using K_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using K_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using K_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_128, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using S_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using S_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using S_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
-using S_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, VITATTN_BF16_SUM_MFMA>;
+using K_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
+using K_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
+using K_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
+using K_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_128, VITATTN_BF16_NW, 64>;
+using S_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
+using S_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
+using S_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
+using S_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
 using K_f32_64 = F32Traits<64, 1, 4, 32>;
 using K_f32_72 = F32Traits<72, 1, 4, 32>;
 using K_f32_80 = F32Traits<80, 1, 4, 32>;

@@ -38,6 +38,8 @@ class Workload:
     std: float = 1.0
     token_factor: tuple[float, float] | None = None  # uniform per-token factor on Q and K
     scale: float | None = None  # None -> 1/sqrt(head_dim)
+    key_ramp: float = 0.0  # > 0: keys drift along a per-head direction (scores rise or fall along a sequence)
+    spikes: int = 0  # keys per sequence pushed far along that direction (a sudden jump of the scores)
 
     @property
     def total_tokens(self) -> int:
@@ -70,9 +72,10 @@ WORKLOADS: dict[str, Workload] = {
 
 
 def custom(lengths, n_heads: int, head_dim: int, dtype: str = BF16, seed: int = 0, std: float = 1.0,
-           token_factor=None, scale: float | None = None, name: str = "custom") -> Workload:
+           token_factor=None, scale: float | None = None, name: str = "custom", key_ramp: float = 0.0,
+           spikes: int = 0) -> Workload:
     return Workload(name, tuple(int(x) for x in lengths), int(n_heads), int(head_dim), dtype, int(seed),
-                    float(std), token_factor, scale)
+                    float(std), token_factor, scale, float(key_ramp), int(spikes))
 
 
 def draw_f32(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -93,6 +96,20 @@ def draw_f32(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
         fk = rng.uniform(lo, hi, size=w.total_tokens).astype(np.float32)
         q *= fq[:, None, None]
         k *= fk[:, None, None]
+    if w.key_ramp > 0.0 or w.spikes > 0:
+        # direction: random signs per head; key j of a sequence of length L moves by
+        # key_ramp * j / L along it, and `spikes` random keys of each sequence by key_ramp more
+        sign = np.where(rng.standard_normal((w.n_heads, w.head_dim)) >= 0, 1.0, -1.0).astype(np.float32)
+        cu = w.cu_seqlens()
+        for s_ in range(len(w.lengths)):
+            a, b = int(cu[s_]), int(cu[s_ + 1])
+            if b <= a:
+                continue
+            pos = (np.arange(b - a, dtype=np.float32) / np.float32(b - a)) * np.float32(w.key_ramp)
+            k[a:b] += pos[:, None, None] * sign[None]
+            if w.spikes > 0:
+                at = rng.integers(a, b, size=w.spikes)
+                k[at] += np.float32(w.key_ramp) * sign[None]
     return q, k, v
 
 

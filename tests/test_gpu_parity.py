@@ -106,13 +106,16 @@ def test_head_independence_bitwise():
     assert torch.equal(got[:, 0], base[:, 0]) and torch.equal(got[:, 2], base[:, 2])
 
 
-@pytest.mark.parametrize("name", ["page-912", "packed-varlen-8"])
+@pytest.mark.parametrize("name", ["page-912", "packed-varlen-8", "f32-mixed"])
 def test_deterministic_bitwise(name):
     # The launch has a fixed schedule (no atomics, no order-dependent reductions), so any
     # run-to-run difference means a race: an LDS buffer reused too early, or a register
     # overwritten while an in-flight matrix instruction still reads it.  page-912 runs the
     # 64-query items, packed-varlen-8 the 256-query ones.
-    w = inputs.WORKLOADS[name]
+    if name == "f32-mixed":
+        w = inputs.custom([700, 300, 45], n_heads=4, head_dim=80, dtype=inputs.F32, seed=31)
+    else:
+        w = inputs.WORKLOADS[name]
     q, k, v, cu, scale = inputs.make(w)
     d = torch.device("cuda:0")
     qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)

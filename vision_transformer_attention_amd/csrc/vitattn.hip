@@ -602,13 +602,25 @@ __device__ __forceinline__ void load_v(VFrag<C>& f, const __bf16* Vs, int kb0, i
 }
 
 // S^T = K.Q^T for 32 keys: S[kb][qb][r] is key kb0+kb*16+4g+r of query row0+qb*16+c.
+// Each chain starts with the 16-deep tail step on a zero accumulator, so that the
+// 16x16x16 MFMA never waits on an accumulator input: on gfx950 a transposing LDS read
+// that lands in the accumulator registers of a 16x16x16 still waiting for a 16x16x32
+// result has been measured to corrupt it.
 template <class C>
 __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K, const bf16x8_t (&Q)[C::QB][C::NK32],
                                       const s16x4_t (&QT)[C::QB]) {
+  if constexpr (C::TAIL) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) S[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < C::QB; ++qb)
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(K.t[kb], QT[qb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) S[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int ks = 0; ks < C::NK32; ++ks)
 #pragma unroll
@@ -616,13 +628,6 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
         S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K.a[kb][ks], Q[qb][ks], S[kb][qb], 0, 0, 0);
-  if constexpr (C::TAIL) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(K.t[kb], QT[qb], S[kb][qb], 0, 0, 0);
-  }
 }
 
 // Softmax weights and O^T += V^T.P^T for one 32-key step.

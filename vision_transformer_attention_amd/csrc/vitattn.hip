@@ -602,10 +602,15 @@ __device__ __forceinline__ void load_v(VFrag<C>& f, const __bf16* Vs, int kb0, i
 }
 
 // S^T = K.Q^T for 32 keys: S[kb][qb][r] is key kb0+kb*16+4g+r of query row0+qb*16+c.
-// Each chain starts with the 16-deep tail step on a zero accumulator, so that the
-// 16x16x16 MFMA never waits on an accumulator input: on gfx950 a transposing LDS read
-// that lands in the accumulator registers of a 16x16x16 still waiting for a 16x16x32
-// result has been measured to corrupt it.
+//
+// head_dim 72 and 80 end the contraction with a 16-deep v_mfma_f32_16x16x16_bf16 (on
+// gfx950 it costs about as much as a 32-deep step, but keeps K rows, Q operands and the
+// DMA at 80 dims instead of 96).  Two hazards of mixing the shapes are kept out by
+// construction: all the 16-deep steps are issued first, on zero accumulators (a 16x16x16
+// waiting for an accumulator input can have it overwritten by a later transposing LDS
+// read), and the 32-deep chains that take their results start only after a scheduling
+// fence and 8 wait states (which the compiler does not insert between MFMAs of different
+// shapes chained through the accumulator).
 template <class C>
 __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K, const bf16x8_t (&Q)[C::QB][C::NK32],
                                       const s16x4_t (&QT)[C::QB]) {
@@ -615,6 +620,9 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
         S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(K.t[kb], QT[qb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)

@@ -874,16 +874,23 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   const int bm = small ? CB::BM : CA::BM;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;  // workgroups go to the 8 XCDs round-robin
   const unsigned row_bytes = (unsigned)n_heads * CA::D * 2u;
   unsigned dma_off[Dma<CA>::PER_WAVE];
   Dma<CA>::init(dma_off, wave, lane, row_bytes);
 
-  // Items in longest-first order are dealt out in rounds of G, alternating direction
-  // (round r, slot s -> item r*G + s, or r*G + G-1-s on odd rounds) to even out the load.
+  // Items in longest-first order are dealt out in rounds of G, alternating direction to
+  // even out the load.  Within a round of m items, XCD x takes the contiguous run
+  // [x*m/8, (x+1)*m/8) (items of one sequence and head share K/V in that XCD's L2), so a
+  // last, partial round still spreads over all XCDs.
   for (int round = 0;; ++round) {
-    const int it = round * G + ((round & 1) ? G - 1 - slot : slot);
-    if (it >= n_items) break;
+    const int base = round * G;
+    if (base >= n_items) break;
+    const int m = min(G, n_items - base);
+    const int lo = (xcd * m) >> 3, cnt = (((xcd + 1) * m) >> 3) - lo;
+    if (xj >= cnt) break;  // only the last round can leave a workgroup without an item
+    const int kk = lo + xj;
+    const int it = base + ((round & 1) ? m - 1 - kk : kk);
     const Item item = map_item(plan, n_seqs, it, bm);
     if (small)
       run_item<CB>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);

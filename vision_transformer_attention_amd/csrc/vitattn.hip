@@ -725,6 +725,9 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
     for (int j = 0; j < 4; ++j)
       W[qb][j] = cvt_pk_bf16(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
                              __builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2 + 1]));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -736,6 +739,9 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
   for (int qb = 0; qb < C::QB; ++qb)
     O[C::NDB][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones),
                                                              __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One 32-key step [kb0, kb0 + 32) of the LDS tile: operand reads, both products, softmax.
@@ -747,7 +753,16 @@ __device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int 
   {
     KFrag<C> kf;
     load_k<C>(kf, Ks, kb0, lane);
+    // Matrix bursts run at raised issue priority: while this wavefront feeds the matrix
+    // pipe, the other wavefront on the SIMD fills the vector slots, instead of both
+    // contending for the pipe in the same phase.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     qk_32<C>(S, kf, Q, QT);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   softmax_pv_32<C, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
 }

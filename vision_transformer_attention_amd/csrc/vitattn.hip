@@ -652,10 +652,11 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
 //
 // Only the FIRST step of an item can hold keys outside the sequence: its first `kinv`
 // keys, which take no part in the max and get weight exactly 0 (also when c2 is 0).
-template <class C, bool FIRST>
+template <class C, bool FIRST, bool PREFETCH = false>
 __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
-                                              int lane) {
+                                              int lane, KFrag<C>* knext = nullptr, const __bf16* Ks = nullptr,
+                                              int kb_next = 0) {
   const int g = lane >> 4;
   if constexpr (FIRST) {
 #pragma unroll
@@ -718,6 +719,7 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
   // latency still hides behind the exponentials.
   VFrag<C> V;
   load_v<C>(V, Vs, kb0, lane);
+  if constexpr (PREFETCH) load_k<C>(*knext, Ks, kb_next, lane);  // the next step's K, same tile
   u32x4_t W[C::QB];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb)
@@ -765,6 +767,23 @@ __device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int 
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax_pv_32<C, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
+}
+
+// A full step whose K fragments were loaded earlier; PREFETCH also loads the next step's
+// (in the same tile) while the exponentials run.
+template <class C, bool PREFETCH>
+__device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, const __bf16* Ks, const __bf16* Vs,
+                                         int kb0, const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                         f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int lane) {
+  f32x4_t S[2][C::QB];
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  qk_32<C>(S, kf, Q, QT);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_pv_32<C, false, PREFETCH>(S, Vs, kb0, O, negM, c2, 0, lane, &knext, Ks, kb0 + C::KSUB);
 }
 
 // One work item (sequence, head, BM queries from q0) for the whole workgroup.  The K/V
@@ -831,20 +850,27 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     const __bf16* Vs = reinterpret_cast<const __bf16*>(stage + C::K_BYTES);
     step_32<C, true>(Ks, Vs, s0 * C::KSUB, pad - s0 * C::KSUB, Q, QT, O, negM, c2, lane);
   }
-  // every later step: full, in order; a new tile starts at each multiple of NSUB
-  const int nsteps = ntiles * C::NSUB;
-  for (int st = s0 + 1; st < nsteps; ++st) {
-    const int t = st / C::NSUB, sub = st % C::NSUB;
-    if (sub == 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
-      __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
-      if (t + 1 < ntiles)
-        Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, 0,
-                                      item.head, n_heads, row_bytes, dma_off, wave, lane);
-    }
+  static_assert(C::NSUB == 2, "tile loop below runs two 32-key steps per tile");
+  if (s0 == 0) {  // tile 0's second step
+    const __bf16* Ks = reinterpret_cast<const __bf16*>(stage);
+    const __bf16* Vs = reinterpret_cast<const __bf16*>(stage + C::K_BYTES);
+    step_32<C, false>(Ks, Vs, C::KSUB, 0, Q, QT, O, negM, c2, lane);
+  }
+  // every later tile: two full steps; the second step's K operands are read while the first
+  // step's exponentials run
+  for (int t = 1; t < ntiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+    __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+    if (t + 1 < ntiles)
+      Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, 0,
+                                    item.head, n_heads, row_bytes, dma_off, wave, lane);
     const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
-    step_32<C, false>(reinterpret_cast<const __bf16*>(buf), reinterpret_cast<const __bf16*>(buf + C::K_BYTES),
-                      sub * C::KSUB, 0, Q, QT, O, negM, c2, lane);
+    const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
+    const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
+    KFrag<C> k0, k1;
+    load_k<C>(k0, Ks, 0, lane);
+    step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+    step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
   }
 
   // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence

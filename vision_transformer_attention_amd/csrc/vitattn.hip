@@ -34,8 +34,9 @@
 //    O^T += V^T.P^T: no data movement between the two products, and the running
 //    output of a query sits in the lane that owns its softmax state, so a rescale
 //    is a per-lane multiply.
-//  * bf16: K/V tiles go HBM -> LDS by global_load_lds_dwordx4 (no VGPRs, no LDS
-//    write instructions), double-buffered, K as [key][d] and V as [key][d] read
+//  * bf16: K/V tiles go HBM -> LDS by buffer_load_dwordx4 ... lds (no VGPRs, no LDS
+//    write instructions; scalar addressing through a buffer resource per tile that
+//    is bounded by the sequence), double-buffered, K as [key][d] and V as [key][d] read
 //    transposed by ds_read_b64_tr_b16, rows padded against bank conflicts.  The
 //    exponent offset of each query row is fixed by the first 32 keys and kept
 //    while no weight reaches 2 (an in-lane max decides, no cross-lane reduction);
@@ -455,8 +456,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 //   V: [BN][VCH chunks of 16 B]  -- natural [key][d] order; read with the transposing
 //      ds_read_b64_tr_b16, whose 4-row x 32-byte footprint per 16 lanes is bank-conflict
 //      free with a row stride of 8 (mod 32) words.
-// Both are filled by global_load_lds_dwordx4: lane l of a wave-wide load lands at
-// base + 16*l, so each wave-wide load fills 64 consecutive chunk slots.
+// Both are filled by buffer_load_dwordx4 with the lds bit: lane l of a wave-wide load
+// lands at base + 16*l, so each wave-wide load fills 64 consecutive chunk slots.
 // ---------------------------------------------------------------------------
 template <int D_, int QB_, int NW_, int BN_>
 struct Bf16Cfg {
@@ -489,6 +490,7 @@ struct Bf16Cfg {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 __device__ __forceinline__ float fbits(unsigned x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ unsigned ubits(float x) { return __builtin_bit_cast(unsigned, x); }
@@ -532,23 +534,27 @@ struct Dma {
 
   // Enqueue the tile whose rows are keys [key0 - lead, key0 - lead + BN): rows before key0
   // (LEAD, the first tile of a sequence whose length is not a multiple of BN) repeat key0.
+  // The loads go through buffer resources based at key0 of this head and bounded by the last
+  // key row of the sequence (key_end - 1), so a lane reads at most that far (an offset past
+  // it would read zeros, never memory outside the sequence).
   template <bool LEAD>
   static __device__ __forceinline__ void issue(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-                                               unsigned char* buf, int key0, int lead, int head, int n_heads,
-                                               unsigned row_bytes, const unsigned (&off)[PER_WAVE], int wave,
-                                               int lane) {
+                                               lds_u8_t* buf, int key0, int key_end, int lead, int head,
+                                               int n_heads, unsigned row_bytes, const unsigned (&off)[PER_WAVE],
+                                               int wave, int lane) {
     const size_t base = ((size_t)key0 * n_heads + head) * C::D;
-    const unsigned char* kb = reinterpret_cast<const unsigned char*>(k + base);
-    const unsigned char* vb = reinterpret_cast<const unsigned char*>(v + base);
+    const unsigned long long extent = (unsigned long long)(key_end - key0 - 1) * row_bytes + C::D * 2;
+    const int n_rec = (int)(extent < 0x7fffffffull ? extent : 0x7fffffffull);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, n_rec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, n_rec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int wl = wave + i * C::NW;
       if (wl < C::LOADS) {
         const bool is_k = wl < C::K_LOADS;
         const unsigned o = LEAD ? lane_offset(wl, lane, lead, row_bytes) : off[i];
-        const unsigned char* src = (is_k ? kb : vb) + o;
-        unsigned char* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+        lds_u8_t* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, (lds_void_t*)dst, 16, o, 0, 0, 0);
       }
     }
   }
@@ -796,7 +802,7 @@ __device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, co
 template <class C>
 __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads, float c2,
-                                         int negate, unsigned char* stage, unsigned row_bytes,
+                                         int negate, lds_u8_t* stage, unsigned row_bytes,
                                          const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const int qend = min(item.q0 + C::BM, item.b);
@@ -807,9 +813,9 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
 
   __syncthreads();  // the previous item is done with both stage buffers
   if (pad > 0)
-    Dma<C>::template issue<true>(k, v, stage, item.a, pad, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, pad, item.head, n_heads, row_bytes, dma_off, wave, lane);
   else
-    Dma<C>::template issue<false>(k, v, stage, item.a, 0, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, item.head, n_heads, row_bytes, dma_off, wave, lane);
 
   // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
   // 16-deep tail dims NK32*32+4g..+4 (zero past D)
@@ -842,18 +848,18 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile 0 has landed
   __syncthreads();                                   // every wave's has
   if (ntiles > 1)
-    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, 0, item.head, n_heads, row_bytes,
+    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, item.b, 0, item.head, n_heads, row_bytes,
                                   dma_off, wave, lane);
   const int s0 = pad / C::KSUB;
   {
-    const __bf16* Ks = reinterpret_cast<const __bf16*>(stage);
-    const __bf16* Vs = reinterpret_cast<const __bf16*>(stage + C::K_BYTES);
+    const __bf16* Ks = (const __bf16*)(stage);
+    const __bf16* Vs = (const __bf16*)(stage + C::K_BYTES);
     step_32<C, true>(Ks, Vs, s0 * C::KSUB, pad - s0 * C::KSUB, Q, QT, O, negM, c2, lane);
   }
   static_assert(C::NSUB == 2, "tile loop below runs two 32-key steps per tile");
   if (s0 == 0) {  // tile 0's second step
-    const __bf16* Ks = reinterpret_cast<const __bf16*>(stage);
-    const __bf16* Vs = reinterpret_cast<const __bf16*>(stage + C::K_BYTES);
+    const __bf16* Ks = (const __bf16*)(stage);
+    const __bf16* Vs = (const __bf16*)(stage + C::K_BYTES);
     step_32<C, false>(Ks, Vs, C::KSUB, 0, Q, QT, O, negM, c2, lane);
   }
   // every later tile: two full steps; the second step's K operands are read while the first
@@ -862,11 +868,11 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
     __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
     if (t + 1 < ntiles)
-      Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, 0,
+      Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, item.b, 0,
                                     item.head, n_heads, row_bytes, dma_off, wave, lane);
-    const unsigned char* buf = stage + (t & 1) * C::STAGE_BYTES;
-    const __bf16* Ks = reinterpret_cast<const __bf16*>(buf);
-    const __bf16* Vs = reinterpret_cast<const __bf16*>(buf + C::K_BYTES);
+    const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
+    const __bf16* Ks = (const __bf16*)(buf);
+    const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
     KFrag<C> k0, k1;
     load_k<C>(k0, Ks, 0, lane);
     step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
@@ -904,7 +910,7 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 "the two query-block sizes share the staging layout");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
-  unsigned char* stage = smem + ((sizeof(PlanLds) + 15) / 16) * 16;
+  lds_u8_t* stage = (lds_u8_t*)smem + ((sizeof(PlanLds) + 15) / 16) * 16;
 
   const int G = gridDim.x;
   int n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CA::BM);
@@ -914,7 +920,9 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CB::BM);
   }
   const int bm = small ? CB::BM : CA::BM;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index and every item field are uniform across a wavefront: keep them in scalar
+  // registers, so that the per-tile DMA issue is scalar address arithmetic
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;  // workgroups go to the 8 XCDs round-robin
   const unsigned row_bytes = (unsigned)n_heads * CA::D * 2u;
   unsigned dma_off[Dma<CA>::PER_WAVE];
@@ -932,7 +940,11 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (xj >= cnt) break;  // only the last round can leave a workgroup without an item
     const int kk = lo + xj;
     const int it = base + ((round & 1) ? m - 1 - kk : kk);
-    const Item item = map_item(plan, n_seqs, it, bm);
+    Item item = map_item(plan, n_seqs, it, bm);
+    item.a = __builtin_amdgcn_readfirstlane(item.a);
+    item.b = __builtin_amdgcn_readfirstlane(item.b);
+    item.head = __builtin_amdgcn_readfirstlane(item.head);
+    item.q0 = __builtin_amdgcn_readfirstlane(item.q0);
     if (small)
       run_item<CB>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);
     else

@@ -516,10 +516,12 @@ struct Dma {
   // tile before `lead` are filled with copies of row `lead`.
   static __device__ __forceinline__ unsigned lane_offset(int wl, int lane, int lead, unsigned row_bytes) {
     const bool is_k = wl < C::K_LOADS;
-    const int z = (is_k ? wl : wl - C::K_LOADS) * 64 + lane;
-    const int per = is_k ? C::KCH : C::VCH;
-    const int row = max(z / per, lead) - lead;
-    const int ch = min(z % per, C::CH - 1);
+    const unsigned z = (unsigned)((is_k ? wl : wl - C::K_LOADS) * 64 + lane);
+    // divisions by the two constant row lengths (the choice is uniform across the wave)
+    const int zr = (int)(is_k ? z / C::KCH : z / C::VCH);
+    const int zc = (int)(is_k ? z % C::KCH : z % C::VCH);
+    const int row = max(zr, lead) - lead;
+    const int ch = min(zc, C::CH - 1);
     return (unsigned)row * row_bytes + (unsigned)ch * 16u;
   }
 
@@ -547,12 +549,17 @@ struct Dma {
     const int n_rec = (int)(extent < 0x7fffffffull ? extent : 0x7fffffffull);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, n_rec, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, n_rec, 0x00020000);
+    // The first tile's offsets are recomputed here each time: an opaque copy of the lane
+    // index keeps the compiler from hoisting their per-lane parts out of the item loop, where
+    // they would take 12 registers for the whole launch (and be spilled).
+    int ln = lane;
+    if constexpr (LEAD) asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int wl = wave + i * C::NW;
       if (wl < C::LOADS) {
         const bool is_k = wl < C::K_LOADS;
-        const unsigned o = LEAD ? lane_offset(wl, lane, lead, row_bytes) : off[i];
+        const unsigned o = LEAD ? lane_offset(wl, ln, lead, row_bytes) : off[i];
         lds_u8_t* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, (lds_void_t*)dst, 16, o, 0, 0, 0);
       }

@@ -17,7 +17,10 @@ the same sequence only.  Sources, by page title:
   segment tables (attention stays inside one image; more images are more segments).
 * "hf2q src/inference/vision/vit_gpu.rs" -- ``vit_attention_gpu`` doc (no mask, the
   ViT is bidirectional; seq-major ``[tokens, heads, head_dim]``) and
-  ``vit_attention_scores_gpu`` doc (the scale is the caller's, 1.0 allowed).
+  ``vit_attention_scores_gpu`` doc (the scale is the caller's, 1.0 allowed);
+  ``vit_repeat_kv_gpu`` doc and its use in ``gemma4v_block_forward_gpu`` (grouped-query
+  attention: K and V carry fewer heads, and query head ``h`` reads K/V head
+  ``h // num_kv_groups``).
 
 Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
 hand-derived golden values, invariants, and a library routine (PyTorch's CPU
@@ -58,6 +61,12 @@ def _bind(lib):
     lib.vitattn_ref_rows_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_double, i64p, ctypes.c_int64]
     lib.vitattn_ref_rows_f64.restype = ctypes.c_int
+    lib.vitattn_ref_fwd_gqa_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
+    lib.vitattn_ref_fwd_gqa_f64.restype = ctypes.c_int
+    lib.vitattn_ref_rows_gqa_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_double, i64p, ctypes.c_int64]
+    lib.vitattn_ref_rows_gqa_f64.restype = ctypes.c_int
     lib.vitattn_ref_row_probs_f64.argtypes = [f32p, f32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_double, ctypes.c_int64, ctypes.c_int32, f64p]
     lib.vitattn_ref_row_probs_f64.restype = ctypes.c_int64
@@ -106,20 +115,31 @@ def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+def _heads(q, k, v):
+    """(T, H, Hkv, D) of q [T, H, D] and k, v [T, Hkv, D], with Hkv a divisor of H."""
+    if q.ndim != 3 or k.shape != v.shape or k.ndim != 3:
+        raise ValueError("q must be [T, H, D] and k, v the same [T, Hkv, D]")
+    t, h, d = q.shape
+    if k.shape[0] != t or k.shape[2] != d or k.shape[1] <= 0 or h % k.shape[1] != 0:
+        raise ValueError("k and v must be [T, Hkv, D] with Hkv dividing H")
+    return t, h, k.shape[1], d
+
+
 def attention(q, k, v, cu_seqlens, scale: float, lib=None) -> np.ndarray:
-    """Full float64 output ``[T, H, D]``; rows outside every sequence stay 0."""
+    """Full float64 output ``[T, H, D]``; rows outside every sequence stay 0.
+
+    k and v may have fewer heads than q (grouped-query attention): query head h
+    uses K/V head h // (H // Hkv)."""
     lib = lib or load()
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     cu = _cu(cu_seqlens)
-    if q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must have the same shape")
-    t, h, d = q.shape
+    t, h, hkv, d = _heads(q, k, v)
     if len(cu) < 1 or cu[0] != 0 or cu[-1] != t or np.any(np.diff(cu) < 0):
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     o = np.zeros((t, h, d), dtype=np.float64)
-    rc = lib.vitattn_ref_fwd_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
-                                 _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, d,
-                                 float(scale))
+    rc = lib.vitattn_ref_fwd_gqa_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                     _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d,
+                                     float(scale))
     if rc != 0:
         raise RuntimeError("oracle failed")
     return o
@@ -130,14 +150,14 @@ def attention_rows(q, k, v, cu_seqlens, scale: float, rows, lib=None) -> np.ndar
     lib = lib or load()
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     cu = _cu(cu_seqlens)
-    t, h, d = q.shape
+    t, h, hkv, d = _heads(q, k, v)
     if len(cu) < 2 or cu[0] != 0 or cu[-1] != t or np.any(np.diff(cu) < 0):
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     r = np.ascontiguousarray(np.asarray(rows), dtype=np.int64)
     o = np.zeros((len(r), h, d), dtype=np.float64)
-    rc = lib.vitattn_ref_rows_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
-                                  _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, d,
-                                  float(scale), _ptr(r, ctypes.c_int64), len(r))
+    rc = lib.vitattn_ref_rows_gqa_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                      _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d,
+                                      float(scale), _ptr(r, ctypes.c_int64), len(r))
     if rc != 0:
         raise RuntimeError("oracle failed (bad rows?)")
     return o

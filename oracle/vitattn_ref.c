@@ -50,17 +50,23 @@
 #endif
 
 /* One query row of one head: writes D outputs to out[0..D).  `w` is caller
- * scratch of at least (b - a) doubles. */
+ * scratch of at least (b - a) doubles.  K and V have n_kv_heads heads (a
+ * divisor of n_heads); query head h reads K/V head h / (n_heads / n_kv_heads),
+ * the grouping of "hf2q src/inference/vision/vit_gpu.rs", doc of
+ * vit_repeat_kv_gpu (each K/V head serves num_kv_groups consecutive query
+ * heads).  n_kv_heads == n_heads is plain multi-head attention. */
 static void ref_one_row(const float* q, const float* k, const float* v,
                         int64_t a, int64_t b, int64_t i, int32_t h,
-                        int32_t n_heads, int32_t head_dim, double scale,
+                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, double scale,
                         double* w, double* out) {
   const int64_t row_stride = (int64_t)n_heads * head_dim;
+  const int64_t kv_stride = (int64_t)n_kv_heads * head_dim;
+  const int32_t hk = h / (n_heads / n_kv_heads);
   const float* qi = q + i * row_stride + (int64_t)h * head_dim;
   /* pass 1: logits and their maximum */
   double m = -INFINITY;
   for (int64_t j = a; j < b; ++j) {
-    const float* kj = k + j * row_stride + (int64_t)h * head_dim;
+    const float* kj = k + j * kv_stride + (int64_t)hk * head_dim;
     double dot = 0.0;
     for (int32_t d = 0; d < head_dim; ++d) dot += (double)qi[d] * (double)kj[d];
     double logit = scale * dot;
@@ -76,7 +82,7 @@ static void ref_one_row(const float* q, const float* k, const float* v,
   }
   for (int32_t e = 0; e < head_dim; ++e) out[e] = 0.0;
   for (int64_t j = a; j < b; ++j) {
-    const float* vj = v + j * row_stride + (int64_t)h * head_dim;
+    const float* vj = v + j * kv_stride + (int64_t)hk * head_dim;
     for (int32_t e = 0; e < head_dim; ++e) out[e] += w[j - a] * (double)vj[e];
   }
   for (int32_t e = 0; e < head_dim; ++e) out[e] /= z;
@@ -91,12 +97,14 @@ int vitattn_ref_threads(void) {
 #endif
 }
 
-/* Full output o[T, H, D] (float64) for q, k, v [T, H, D] (float32 values).
- * Returns 0, or -1 on a bad argument or an allocation failure. */
-int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* o,
-                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
-                        int32_t head_dim, double scale) {
+/* Full output o[T, H, D] (float64) for q [T, H, D] and k, v [T, Hkv, D]
+ * (float32 values), Hkv a divisor of H.  Returns 0, or -1 on a bad argument or
+ * an allocation failure. */
+int vitattn_ref_fwd_gqa_f64(const float* q, const float* k, const float* v, double* o,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_dim, double scale) {
   if (n_seqs < 0 || n_heads <= 0 || head_dim <= 0) return -1;
+  if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return -1;
   if (n_seqs == 0) return 0;
   if (!q || !k || !v || !o || !cu_seqlens) return -1;
   int64_t max_len = 0;
@@ -119,7 +127,7 @@ int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* 
         int32_t s = (int32_t)(p / n_heads), h = (int32_t)(p % n_heads);
         int64_t a = cu_seqlens[s], b = cu_seqlens[s + 1];
         for (int64_t i = a; i < b; ++i)
-          ref_one_row(q, k, v, a, b, i, h, n_heads, head_dim, scale, w,
+          ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, w,
                       o + (i * n_heads + h) * (int64_t)head_dim);
       }
       free(w);
@@ -128,13 +136,22 @@ int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* 
   return failed ? -1 : 0;
 }
 
+/* Multi-head attention (as many K/V heads as query heads). */
+int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* o,
+                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                        int32_t head_dim, double scale) {
+  return vitattn_ref_fwd_gqa_f64(q, k, v, o, cu_seqlens, n_seqs, n_heads, n_heads, head_dim, scale);
+}
+
 /* Output for a chosen set of token rows only: o_rows[n_rows, H, D] (float64),
  * rows[r] a global token index in [0, T).  Used where the full output would
  * take too long.  Returns 0, or -1 on a bad argument. */
-int vitattn_ref_rows_f64(const float* q, const float* k, const float* v, double* o_rows,
-                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
-                         int32_t head_dim, double scale, const int64_t* rows, int64_t n_rows) {
+int vitattn_ref_rows_gqa_f64(const float* q, const float* k, const float* v, double* o_rows,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                             int32_t n_kv_heads, int32_t head_dim, double scale,
+                             const int64_t* rows, int64_t n_rows) {
   if (n_seqs <= 0 || n_heads <= 0 || head_dim <= 0 || n_rows < 0) return -1;
+  if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return -1;
   if (!q || !k || !v || !o_rows || !cu_seqlens || (n_rows > 0 && !rows)) return -1;
   const int64_t total = cu_seqlens[n_seqs];
   int64_t max_len = 0;
@@ -161,13 +178,20 @@ int vitattn_ref_rows_f64(const float* q, const float* k, const float* v, double*
         /* the sequence that holds row i: the last s with cu[s] <= i < cu[s+1] */
         int32_t s = 0;
         while (!(cu_seqlens[s] <= i && i < cu_seqlens[s + 1])) ++s;
-        ref_one_row(q, k, v, cu_seqlens[s], cu_seqlens[s + 1], i, h, n_heads, head_dim,
-                    scale, w, o_rows + (r * n_heads + h) * (int64_t)head_dim);
+        ref_one_row(q, k, v, cu_seqlens[s], cu_seqlens[s + 1], i, h, n_heads, n_kv_heads,
+                    head_dim, scale, w, o_rows + (r * n_heads + h) * (int64_t)head_dim);
       }
       free(w);
     }
   }
   return failed ? -1 : 0;
+}
+
+int vitattn_ref_rows_f64(const float* q, const float* k, const float* v, double* o_rows,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                         int32_t head_dim, double scale, const int64_t* rows, int64_t n_rows) {
+  return vitattn_ref_rows_gqa_f64(q, k, v, o_rows, cu_seqlens, n_seqs, n_heads, n_heads, head_dim,
+                                  scale, rows, n_rows);
 }
 
 /* The attention weights of one (token row, head): p_out[j - a] for the keys j

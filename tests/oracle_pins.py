@@ -202,9 +202,56 @@ def pin_rows_match_full(lib):
     assert np.array_equal(got, full[rows])
 
 
+def _rand_gqa(lengths, h, hkv, d, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    t = int(sum(lengths))
+    q = (rng.standard_normal((t, h, d)) * std).astype(np.float32)
+    k = (rng.standard_normal((t, hkv, d)) * std).astype(np.float32)
+    v = rng.standard_normal((t, hkv, d)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def pin_gqa_is_repeated_kv(lib):
+    # grouped-query attention is multi-head attention on K/V whose head g is copied to the
+    # H/Hkv consecutive query heads g*(H/Hkv) .. (g+1)*(H/Hkv)-1 ("hf2q ... vit_gpu.rs",
+    # vit_repeat_kv_gpu doc); the copies are made here with numpy, outside the oracle
+    for h, hkv in ((8, 2), (6, 3), (4, 1), (5, 5)):
+        q, k, v, cu = _rand_gqa([9, 1, 23], h, hkv, 10, seed=26 + h + hkv, std=1.3)
+        got = oracle.attention(q, k, v, cu, 0.37, lib=lib)
+        ref = oracle.attention(q, np.repeat(k, h // hkv, axis=1), np.repeat(v, h // hkv, axis=1), cu, 0.37, lib=lib)
+        assert np.array_equal(got, ref)
+        rows = np.array([0, 8, 9, 10, 32], np.int64)
+        assert np.array_equal(oracle.attention_rows(q, k, v, cu, 0.37, rows, lib=lib), ref[rows])
+
+
+def pin_gqa_torch_sdpa(lib):
+    # PyTorch's CPU SDPA in float64 with its own grouped-query mode
+    import torch
+    import torch.nn.functional as F
+    q, k, v, cu = _rand_gqa([31, 4, 50], 8, 2, 16, seed=27, std=1.4)
+    got = oracle.attention(q, k, v, cu, 0.29, lib=lib)
+    for a, b in _segments(cu):
+        t = lambda x: torch.from_numpy(x[a:b].astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+        ref = F.scaled_dot_product_attention(t(q), t(k), t(v), scale=0.29, enable_gqa=True)
+        ref = ref.squeeze(0).permute(1, 0, 2).numpy()
+        assert np.allclose(got[a:b], ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_gqa_constant_v_per_group(lib):
+    # every key of K/V head g holding the value c_g makes every query head of group g output c_g
+    q, k, v, cu = _rand_gqa([7, 19], 6, 3, 5, seed=28)
+    for g in range(3):
+        v[:, g, :] = np.float32(g + 0.25)
+    got = oracle.attention(q, k, v, cu, 0.8, lib=lib)
+    for h in range(6):
+        assert np.allclose(got[:, h, :], h // 2 + 0.25, rtol=0, atol=1e-13)
+
+
 PINS = [
     pin_golden, pin_scale_one_logistic, pin_single_key, pin_constant_v, pin_uniform_when_no_signal,
     pin_weights_are_a_distribution, pin_key_shift_invariance, pin_key_permutation_invariance,
     pin_affine_in_v, pin_convex_hull, pin_block_diagonal, pin_head_independence,
     pin_head_dim_zero_padding, pin_torch_sdpa, pin_rows_match_full,
+    pin_gqa_is_repeated_kv, pin_gqa_torch_sdpa, pin_gqa_constant_v_per_group,
 ]

@@ -22,22 +22,26 @@ MUTANTS = {
     "value-is-key": [("const float* vj = v + ", "const float* vj = k + ")],
     "query-head-ignored": [("const float* qi = q + i * row_stride + (int64_t)h * head_dim;",
                             "const float* qi = q + i * row_stride;")],
-    "key-head-ignored": [("const float* kj = k + j * row_stride + (int64_t)h * head_dim;\n    double dot",
-                          "const float* kj = k + j * row_stride;\n    double dot")],
+    "key-head-ignored": [("const float* kj = k + j * kv_stride + (int64_t)hk * head_dim;\n    double dot",
+                          "const float* kj = k + j * kv_stride;\n    double dot")],
+    "kv-head-modulo": [("const int32_t hk = h / (n_heads / n_kv_heads);",
+                        "const int32_t hk = h % n_kv_heads;")],
+    "kv-stride-is-query-stride": [("const int64_t kv_stride = (int64_t)n_kv_heads * head_dim;",
+                                   "const int64_t kv_stride = (int64_t)n_heads * head_dim;")],
     "no-normalisation": [("for (int32_t e = 0; e < head_dim; ++e) out[e] /= z;",
                           "for (int32_t e = 0; e < head_dim; ++e) out[e] /= 1.0;")],
     "keys-cross-images": [
         ("double* w = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));",
          "double* w = (double*)malloc(sizeof(double) * (size_t)(cu_seqlens[n_seqs] + 1));"),
-        ("ref_one_row(q, k, v, a, b, i, h, n_heads, head_dim, scale, w,\n                      o + (i * n_heads",
-         "ref_one_row(q, k, v, 0, cu_seqlens[n_seqs], i, h, n_heads, head_dim, scale, w,\n                      o + (i * n_heads"),
+        ("ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, w,\n                      o + (i * n_heads",
+         "ref_one_row(q, k, v, 0, cu_seqlens[n_seqs], i, h, n_heads, n_kv_heads, head_dim, scale, w,\n                      o + (i * n_heads"),
     ],
     "last-key-dropped": [("for (int64_t j = a; j < b; ++j) {\n    const float* kj",
                           "for (int64_t j = a; j < b - 1; ++j) {\n    const float* kj")],
     "max-subtracted-from-one-key": [("double wj = exp(w[j - a] - m);", "double wj = exp(w[j - a] - (j == a ? m : 0.0));")],
     "sum-misses-first-key": [("    z += wj;\n", "    if (j > a) z += wj;\n")],
-    "value-head-ignored": [("const float* vj = v + j * row_stride + (int64_t)h * head_dim;",
-                            "const float* vj = v + j * row_stride;")],
+    "value-head-ignored": [("const float* vj = v + j * kv_stride + (int64_t)hk * head_dim;",
+                            "const float* vj = v + j * kv_stride;")],
 }
 
 RUNNER = r"""

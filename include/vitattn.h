@@ -20,8 +20,9 @@
  *
  * For every sequence s in [0, n_seqs), every head h and every token row
  * i in [cu_seqlens[s], cu_seqlens[s+1]):
- *     o[i,h,:] = sum_j softmax_j(scale * q[i,h,:] . k[j,h,:]) * v[j,h,:]
- * with j over the same range [cu_seqlens[s], cu_seqlens[s+1]).
+ *     o[i,h,:] = sum_j softmax_j(scale * q[i,h,:] . k[j,g,:]) * v[j,g,:]
+ * with j over the same range [cu_seqlens[s], cu_seqlens[s+1]), and g = h
+ * (vitattn_fwd) or g = h / (n_heads / n_kv_heads) (vitattn_fwd_gqa).
  */
 #ifndef VITATTN_H
 #define VITATTN_H
@@ -82,6 +83,30 @@ typedef enum {
 int vitattn_fwd(const void* q, const void* k, const void* v, void* o,
                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
                 int32_t head_dim, float scale, int32_t dtype, hipStream_t stream);
+
+/*
+ * vitattn_fwd_gqa -- the same forward pass with grouped-query attention: k and
+ * v carry n_kv_heads heads, a divisor of n_heads, and query head h attends
+ * with K/V head h / (n_heads / n_kv_heads).  This is the grouping of "hf2q
+ * src/inference/vision/vit_gpu.rs", doc of vit_repeat_kv_gpu, used by
+ * gemma4v_block_forward_gpu to widen K and V to the query heads before
+ * attention; here the K/V heads are read in place and never copied.
+ *
+ * q, o    : as for vitattn_fwd, [T, n_heads, head_dim].
+ * k, v    : DEVICE pointers, contiguous [T, n_kv_heads, head_dim] of `dtype`,
+ *           16-byte aligned.  Read only.
+ * n_kv_heads : > 0 and a divisor of n_heads (else VITATTN_ERR_INVALID_ARG,
+ *           before any HIP call).  n_kv_heads == n_heads is vitattn_fwd;
+ *           n_kv_heads == 1 is multi-query attention.
+ * Every other argument, the validation order, the asynchrony and the error
+ * behaviour are those of vitattn_fwd.  For each (sequence, query head) the
+ * result is bitwise that of vitattn_fwd on K/V whose head h holds K/V head
+ * h / (n_heads / n_kv_heads).
+ */
+int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
+                    const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                    int32_t n_kv_heads, int32_t head_dim, float scale, int32_t dtype,
+                    hipStream_t stream);
 
 /* Static, never-NULL description of a status code. */
 const char* vitattn_status_string(int status);

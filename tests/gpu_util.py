@@ -64,7 +64,7 @@ def sample_rows(cu: np.ndarray, bm: int = 128, extra: int = 6, seed: int = 0) ->
 
 def check_workload(w: inputs.Workload, full: bool, rows=None):
     say(f"[parity] {w.name}: lengths={list(w.lengths)[:10]}{'...' if len(w.lengths) > 10 else ''} "
-        f"H={w.n_heads} D={w.head_dim} {w.dtype} seed={w.seed} full={full}")
+        f"H={w.n_heads} Hkv={w.kv_heads} D={w.head_dim} {w.dtype} seed={w.seed} full={full}")
     q, k, v, cu, scale = inputs.make(w)
     o = run_gpu(q, k, v, cu, scale)
     assert torch.isfinite(o.float()).all()

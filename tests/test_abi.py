@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["vitattn_fwd", "vitattn_status_string", "vitattn_last_error", "vitattn_kernel_config"])
+        ["vitattn_fwd", "vitattn_fwd_gqa", "vitattn_status_string", "vitattn_last_error", "vitattn_kernel_config"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -79,6 +79,26 @@ def test_validation_before_any_hip_call(lib, args, status):
     a.update(args)
     rc = lib.vitattn_fwd(a["q"], a["k"], a["v"], a["o"], a["cu"], a["n_seqs"], a["n_heads"], a["head_dim"],
                          ctypes.c_float(a["scale"]), a["dtype"], None)
+    assert rc == status
+    if status != OK:
+        assert len(lib.vitattn_last_error()) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(n_kv_heads=0), INVALID),
+    (dict(n_kv_heads=-1), INVALID),
+    (dict(n_kv_heads=3), INVALID),      # not a divisor of 8 query heads
+    (dict(n_kv_heads=16), INVALID),     # more K/V heads than query heads
+    (dict(n_kv_heads=2, head_dim=96), BAD_HD),
+    (dict(n_kv_heads=2, q=FAKE + 4), INVALID),
+    (dict(n_kv_heads=2, n_seqs=0), OK),
+])
+def test_gqa_validation_before_any_hip_call(lib, args, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, cu=FAKE, n_seqs=1, n_heads=8, n_kv_heads=2, head_dim=80, scale=0.1,
+             dtype=1)
+    a.update(args)
+    rc = lib.vitattn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["cu"], a["n_seqs"], a["n_heads"], a["n_kv_heads"],
+                             a["head_dim"], ctypes.c_float(a["scale"]), a["dtype"], None)
     assert rc == status
     if status != OK:
         assert len(lib.vitattn_last_error()) > 0

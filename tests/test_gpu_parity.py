@@ -144,3 +144,36 @@ def test_constant_v_gives_constant_output():
     v = torch.full_like(v, 1.5)
     o = run_gpu(q, k, v, cu, scale)
     assert float((o.float() - 1.5).abs().max()) <= 1e-2
+
+
+# ---- grouped-query attention (K/V with a divisor of the query heads) ----
+
+@pytest.mark.parametrize("dtype,head_dim,h,hkv", [(inputs.BF16, 64, 8, 2), (inputs.BF16, 72, 6, 3),
+                                                  (inputs.BF16, 80, 8, 1), (inputs.BF16, 128, 8, 4),
+                                                  (inputs.F32, 64, 4, 2), (inputs.F32, 80, 6, 1)])
+def test_grouped_query_edge_lengths(dtype, head_dim, h, hkv):
+    lengths = [1, 31, 64, 65, 129, 300]
+    w = inputs.custom(lengths, n_heads=h, head_dim=head_dim, dtype=dtype, seed=200 + head_dim + hkv, n_kv_heads=hkv)
+    check_workload(w, full=True)
+
+
+def test_grouped_query_rising_scores():
+    w = inputs.custom([1000, 64, 5], n_heads=8, head_dim=80, dtype=inputs.BF16, seed=29, key_ramp=300.0, spikes=2,
+                      n_kv_heads=2)
+    check_workload(w, full=True)
+
+
+def test_grouped_query_packed_sampled_rows():
+    check_workload(inputs.WORKLOADS["packed-varlen-8-gqa4"], full=False)
+
+
+@pytest.mark.parametrize("dtype", [inputs.BF16, inputs.F32])
+def test_grouped_query_equals_repeated_kv_bitwise(dtype):
+    # reading K/V head h // g in place gives bitwise the multi-head result on K/V widened by copying
+    w = inputs.custom([300, 77, 1000, 1], n_heads=8, head_dim=80, dtype=dtype, seed=30, n_kv_heads=2)
+    q, k, v, cu, scale = inputs.make(w)
+    say(f"[parity] gqa vs repeated kv: {w.lengths} H=8 Hkv=2 {dtype}")
+    o_gqa = run_gpu(q, k, v, cu, scale)
+    o_mha = run_gpu(q, k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous(), cu,
+                    scale)
+    assert torch.equal(o_gqa, o_mha)

@@ -48,3 +48,13 @@ def test_page_workload_widens_logits():
     q, k, _ = inputs.draw_f32(w)
     norms = np.linalg.norm(q.reshape(q.shape[0], -1), axis=1) / np.sqrt(q.shape[1] * q.shape[2])
     assert norms.min() < 0.7 and norms.max() > 1.6
+
+
+def test_gqa_workload_draws_fewer_kv_heads():
+    w = inputs.WORKLOADS["packed-varlen-8-gqa4"]
+    q, k, v = inputs.draw_f32(w)
+    assert q.shape == (w.total_tokens, 16, 80) and k.shape == v.shape == (w.total_tokens, 4, 80)
+    assert w.kv_heads == 4 and inputs.WORKLOADS["packed-varlen-8"].kv_heads == 16
+    # the query draw is the plain one: the seeded stream starts with Q
+    rng = np.random.default_rng(w.seed)
+    assert np.array_equal(q, rng.standard_normal(q.shape, dtype=np.float32))

@@ -45,6 +45,8 @@ def load_library(path: str | None = None):
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.vitattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float, i32, vp]
     lib.vitattn_fwd.restype = ctypes.c_int
+    lib.vitattn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp]
+    lib.vitattn_fwd_gqa.restype = ctypes.c_int
     lib.vitattn_status_string.argtypes = [ctypes.c_int]
     lib.vitattn_status_string.restype = ctypes.c_char_p
     lib.vitattn_last_error.argtypes = []
@@ -105,14 +107,24 @@ def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_seqs:
                                 ctypes.c_float(scale), dtype_code, stream))
 
 
+def fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_seqs: int, n_heads: int,
+                n_kv_heads: int, head_dim: int, scale: float, dtype_code: int, stream: int) -> None:
+    """Direct call of the grouped-query C entry point with raw pointers."""
+    lib = load_library()
+    _check(lib, lib.vitattn_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, cu_ptr, n_seqs, n_heads, n_kv_heads, head_dim,
+                                    ctypes.c_float(scale), dtype_code, stream))
+
+
 def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True):
     """Bidirectional attention over packed sequences; returns ``o`` like ``q``.
 
-    q, k, v: contiguous CUDA (HIP) tensors ``[T, H, D]`` of one dtype (bfloat16 or
-    float32), D in {64, 72, 80, 128}.  cu_seqlens: int32 ``[n_seqs + 1]`` prefix
-    array on the same device (a CPU copy is checked on the host when
-    ``check_cu``).  scale defaults to ``1/sqrt(D)``; any finite value (1.0
-    included) is passed through unchanged.
+    q: contiguous CUDA (HIP) tensor ``[T, H, D]`` of bfloat16 or float32, D in
+    {64, 72, 80, 128}; k, v: the same dtype, ``[T, Hkv, D]`` with Hkv dividing H
+    (Hkv < H is grouped-query attention: query head h uses K/V head
+    ``h // (H // Hkv)``).  cu_seqlens: int32 ``[n_seqs + 1]`` prefix array on the
+    same device (a CPU copy is checked on the host when ``check_cu``).  scale
+    defaults to ``1/sqrt(D)``; any finite value (1.0 included) is passed through
+    unchanged.
     """
     import torch
     lib = load_library()
@@ -125,8 +137,10 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
             raise ValueError(f"{name} must be [tokens, heads, head_dim]")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k and v must have the same shape")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or k.shape[1] <= 0 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("k and v must be [T, Hkv, D] with the tokens and head_dim of q and Hkv dividing q's heads")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k and v must have the same dtype")
     if q.device != k.device or q.device != v.device:
@@ -155,6 +169,11 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
         return out
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs, n_heads,
-                head_dim, float(scale), code, stream)
+        n_kv_heads = k.shape[1]
+        if n_kv_heads == n_heads:
+            fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs, n_heads,
+                    head_dim, float(scale), code, stream)
+        else:
+            fwd_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs,
+                        n_heads, n_kv_heads, head_dim, float(scale), code, stream)
     return out

@@ -316,8 +316,9 @@ template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const typename T::elem_t* __restrict__ q, const typename T::elem_t* __restrict__ k,
     const typename T::elem_t* __restrict__ v, typename T::elem_t* __restrict__ o,
-    const int32_t* __restrict__ cu, int n_seqs, int n_heads, float c2, int negate) {
+    const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2, int negate) {
   using elem_t = typename T::elem_t;
+  const int kv_group = n_heads / n_kv_heads;  // query heads per K/V head
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
   elem_t* stage = reinterpret_cast<elem_t*>(smem + ((sizeof(PlanLds) + 15) / 16) * 16);
@@ -349,14 +350,15 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const int ntiles = ceil_div(item.b - item.a, T::BN);
     typename T::Pre pre;
     __syncthreads();  // the previous item is done with both stage buffers
-    T::fetch(pre, k, v, item.a, item.b, item.head, n_heads);
+    const int kv_head = item.head / kv_group;
+    T::fetch(pre, k, v, item.a, item.b, kv_head, n_kv_heads);
     T::store(pre, stage);
 
     for (int t = 0; t < ntiles; ++t) {
       __syncthreads();  // tile t is in LDS; buffer (t+1)&1 is free
       const elem_t* cur = stage + (t & 1) * T::STAGE_ELEMS;
       const int key0 = item.a + t * T::BN;
-      if (t + 1 < ntiles) T::fetch(pre, k, v, key0 + T::BN, item.b, item.head, n_heads);
+      if (t + 1 < ntiles) T::fetch(pre, k, v, key0 + T::BN, item.b, kv_head, n_kv_heads);
 
       f32x4_t S[T::NKB][T::QB];
       T::qk(S, Q, cur, lane);
@@ -808,10 +810,12 @@ __device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, co
 // are masked in the first step, and every later step is a full one.
 template <class C>
 __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                         const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads, float c2,
-                                         int negate, lds_u8_t* stage, unsigned row_bytes,
-                                         const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave, int lane) {
+                                         const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads,
+                                         int n_kv_heads, int kv_group, float c2, int negate, lds_u8_t* stage,
+                                         unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave,
+                                         int lane) {
   const int g = lane >> 4, c = lane & 15;
+  const int kv_head = item.head / kv_group;  // K/V rows are [T, n_kv_heads, D]
   const int qend = min(item.q0 + C::BM, item.b);
   const int row0 = item.q0 + wave * C::NQ;
   const int ntiles = ceil_div(item.b - item.a, C::BN);
@@ -820,9 +824,9 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
 
   __syncthreads();  // the previous item is done with both stage buffers
   if (pad > 0)
-    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, pad, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, pad, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
   else
-    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, item.head, n_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
 
   // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
   // 16-deep tail dims NK32*32+4g..+4 (zero past D)
@@ -855,7 +859,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile 0 has landed
   __syncthreads();                                   // every wave's has
   if (ntiles > 1)
-    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, item.b, 0, item.head, n_heads, row_bytes,
+    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, item.b, 0, kv_head, n_kv_heads, row_bytes,
                                   dma_off, wave, lane);
   const int s0 = pad / C::KSUB;
   {
@@ -876,7 +880,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
     if (t + 1 < ntiles)
       Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, item.b, 0,
-                                    item.head, n_heads, row_bytes, dma_off, wave, lane);
+                                    kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
     const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
     const __bf16* Ks = (const __bf16*)(buf);
     const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
@@ -912,7 +916,8 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
 template <class CA, class CB>
 __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, float c2, int negate) {
+    __bf16* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2,
+    int negate) {
   static_assert(CA::D == CB::D && CA::NW == CB::NW && CA::BN == CB::BN && CA::STAGE_BYTES == CB::STAGE_BYTES,
                 "the two query-block sizes share the staging layout");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -931,7 +936,8 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // registers, so that the per-tile DMA issue is scalar address arithmetic
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;  // workgroups go to the 8 XCDs round-robin
-  const unsigned row_bytes = (unsigned)n_heads * CA::D * 2u;
+  const unsigned row_bytes = (unsigned)n_kv_heads * CA::D * 2u;  // one K/V row
+  const int kv_group = n_heads / n_kv_heads;                       // query heads per K/V head
   unsigned dma_off[Dma<CA>::PER_WAVE];
   Dma<CA>::init(dma_off, wave, lane, row_bytes);
 
@@ -953,9 +959,9 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     item.head = __builtin_amdgcn_readfirstlane(item.head);
     item.q0 = __builtin_amdgcn_readfirstlane(item.q0);
     if (small)
-      run_item<CB>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);
+      run_item<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave, lane);
     else
-      run_item<CA>(item, q, k, v, o, n_heads, c2, negate, stage, row_bytes, dma_off, wave, lane);
+      run_item<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave, lane);
   }
 }
 
@@ -1156,11 +1162,15 @@ int vitattn_kernel_config(int32_t head_dim, int32_t dtype, int32_t* block_m, int
   return VITATTN_OK;
 }
 
-int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t n_seqs,
-                int32_t n_heads, int32_t head_dim, float scale, int32_t dtype, hipStream_t stream) {
+int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                    int32_t n_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                    int32_t dtype, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (n_seqs < 0) return fail(VITATTN_ERR_INVALID_ARG, "n_seqs must be >= 0 (got %d)", n_seqs);
   if (n_heads <= 0) return fail(VITATTN_ERR_INVALID_ARG, "n_heads must be > 0 (got %d)", n_heads);
+  if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
+    return fail(VITATTN_ERR_INVALID_ARG, "n_kv_heads must be a positive divisor of n_heads (got %d for %d heads)",
+                n_kv_heads, n_heads);
   int rc = validate(head_dim, dtype);
   if (rc != VITATTN_OK) return rc;
   if (!std::isfinite(scale)) return fail(VITATTN_ERR_INVALID_ARG, "scale must be finite");
@@ -1188,7 +1198,8 @@ int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int3
       const __bf16* vv = static_cast<const __bf16*>(v);
       __bf16* oo = static_cast<__bf16*>(o);
       const int32_t* cc = cu_seqlens + s0;
-      void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&c2, (void*)&negate};
+      void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&n_kv_heads,
+                      (void*)&c2, (void*)&negate};
       hipError_t e = hipLaunchKernel(d.func, dim3(st->grid[idx]), dim3(d.nt), args, d.lds, stream);
       if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     } else {
@@ -1197,7 +1208,8 @@ int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int3
       const float* vv = static_cast<const float*>(v);
       float* oo = static_cast<float*>(o);
       const int32_t* cc = cu_seqlens + s0;
-      void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&c2, (void*)&negate};
+      void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&n_kv_heads,
+                      (void*)&c2, (void*)&negate};
       hipError_t e = hipLaunchKernel(d.func, dim3(st->grid[idx]), dim3(d.nt), args, d.lds, stream);
       if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     }
@@ -1205,6 +1217,11 @@ int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int3
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "after launch: %s", hipGetErrorString(e));
   return VITATTN_OK;
+}
+
+int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t n_seqs,
+                int32_t n_heads, int32_t head_dim, float scale, int32_t dtype, hipStream_t stream) {
+  return vitattn_fwd_gqa(q, k, v, o, cu_seqlens, n_seqs, n_heads, n_heads, head_dim, scale, dtype, stream);
 }
 
 }  // extern "C"

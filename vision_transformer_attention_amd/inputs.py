@@ -5,8 +5,9 @@ oracle's tests.  It only draws random numbers and lays them out; it holds none
 of the attention arithmetic.
 
 Recipe (every workload): ``numpy.random.default_rng(seed)`` (PCG64) draws float32
-``standard_normal`` arrays in the fixed order Q, K, V, each ``[T, H, D]`` row-major
-(seq-major tokens, then heads, then head_dim), then any per-token factors.  bf16
+``standard_normal`` arrays in the fixed order Q, K, V, row-major ``[T, H, D]`` for Q
+and ``[T, Hkv, D]`` for K and V (seq-major tokens, then heads, then head_dim; Hkv = H
+except for grouped-query workloads), then any per-token factors.  bf16
 tensors are the float32 draws rounded to nearest-even by ``torch.Tensor.to``.
 The sequence-length prefix array ``cu_seqlens`` is int32 ``[n_seqs + 1]``.
 
@@ -40,6 +41,11 @@ class Workload:
     scale: float | None = None  # None -> 1/sqrt(head_dim)
     key_ramp: float = 0.0  # > 0: keys drift along a per-head direction (scores rise or fall along a sequence)
     spikes: int = 0  # keys per sequence pushed far along that direction (a sudden jump of the scores)
+    n_kv_heads: int | None = None  # K/V heads (a divisor of n_heads); None -> n_heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads if self.n_kv_heads is not None else self.n_heads
 
     @property
     def total_tokens(self) -> int:
@@ -68,23 +74,27 @@ WORKLOADS: dict[str, Workload] = {
     "page-912": Workload("page-912", (912,), 16, 80, BF16, seed=3, token_factor=(0.5, 2.0)),
     "packed-varlen-8": Workload("packed-varlen-8", PACKED_LENGTHS, 16, 80, BF16, seed=4),
     "long-16384": Workload("long-16384", (16384,), 16, 128, BF16, seed=5),
+    # grouped-query attention: the packed batch with 4 K/V heads for the 16 query heads
+    "packed-varlen-8-gqa4": Workload("packed-varlen-8-gqa4", PACKED_LENGTHS, 16, 80, BF16, seed=6, n_kv_heads=4),
 }
 
 
 def custom(lengths, n_heads: int, head_dim: int, dtype: str = BF16, seed: int = 0, std: float = 1.0,
            token_factor=None, scale: float | None = None, name: str = "custom", key_ramp: float = 0.0,
-           spikes: int = 0) -> Workload:
+           spikes: int = 0, n_kv_heads: int | None = None) -> Workload:
     return Workload(name, tuple(int(x) for x in lengths), int(n_heads), int(head_dim), dtype, int(seed),
-                    float(std), token_factor, scale, float(key_ramp), int(spikes))
+                    float(std), token_factor, scale, float(key_ramp), int(spikes),
+                    None if n_kv_heads is None else int(n_kv_heads))
 
 
 def draw_f32(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """The float32 draws (before any bf16 rounding), each ``[T, H, D]``."""
+    """The float32 draws (before any bf16 rounding): q ``[T, H, D]``, k and v ``[T, Hkv, D]``."""
     rng = np.random.default_rng(w.seed)
     shape = (w.total_tokens, w.n_heads, w.head_dim)
+    kv_shape = (w.total_tokens, w.kv_heads, w.head_dim)
     q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
+    v = rng.standard_normal(kv_shape, dtype=np.float32)
     if w.std != 1.0:
         s = np.float32(w.std)
         q *= s
@@ -99,7 +109,7 @@ def draw_f32(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     if w.key_ramp > 0.0 or w.spikes > 0:
         # direction: random signs per head; key j of a sequence of length L moves by
         # key_ramp * j / L along it, and `spikes` random keys of each sequence by key_ramp more
-        sign = np.where(rng.standard_normal((w.n_heads, w.head_dim)) >= 0, 1.0, -1.0).astype(np.float32)
+        sign = np.where(rng.standard_normal((w.kv_heads, w.head_dim)) >= 0, 1.0, -1.0).astype(np.float32)
         cu = w.cu_seqlens()
         for s_ in range(len(w.lengths)):
             a, b = int(cu[s_]), int(cu[s_ + 1])

@@ -21,7 +21,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (and f16) MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32
 HEADLINE = "packed-varlen-8"
 SECONDARY = "page-912"
 PROFILES = os.path.join(ROOT, "profiles")
@@ -31,7 +32,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_workload(name: str, steps: int, warmup: int):
+def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False):
     import torch
 
     import vision_transformer_attention_amd as vta
@@ -41,7 +42,7 @@ def time_workload(name: str, steps: int, warmup: int):
     q, k, v, cu, scale = inputs.make(w)
     dev = torch.device("cuda:0")
     q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         vta.fwd(q, k, v, cu, scale, out=out, check_cu=False)
@@ -124,6 +125,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-secondary", action="store_true", help="time only --workload (for profiling runs)")
+    ap.add_argument("--out-dtype", choices=("same", "f32"), default="same",
+                    help="output element type: the input's, or float32 (16-bit inputs only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -137,7 +140,7 @@ def main():
         sys.exit(1)
 
     log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
-    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup)
+    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup, args.out_dtype == "f32")
     tflops = w.flops / (kernel_ms * 1e-3) / 1e12
     log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
     if args.copy_calibration_mib > 0:
@@ -161,7 +164,8 @@ def main():
         log("[bench] timing the float64 oracle on the host cores (bounded sample)")
         cpu = cpu_baseline(args.workload)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
-    dtype = "bf16" if w.dtype == "bf16" else "f32"
+    dtype = w.dtype  # the element type the products are computed in: "bf16", "f16" or "f32"
+    peak = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS  # dense f16 MFMA = dense bf16
     rec = {
         "metric": "attention TFLOP/s (4*S^2*D*H summed over sequences)",
         "value": tflops,
@@ -178,12 +182,13 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {
             "workload": w.name, "lengths": list(w.lengths), "tokens": w.total_tokens, "heads": w.n_heads,
-            "head_dim": w.head_dim, "flops_per_step": w.flops, "block_m": cfg["block_m"],
+            "head_dim": w.head_dim, "kv_heads": w.kv_heads, "out_dtype": "f32" if args.out_dtype == "f32" else w.dtype,
+            "flops_per_step": w.flops, "block_m": cfg["block_m"],
             "block_n": cfg["block_n"], "waves_per_workgroup": cfg["waves"], "grid": cfg["grid"],
         },
         "roofline": {
-            "bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": tflops / BF16_PEAK_TFLOPS, "traffic": load_traffic(w.name),
+            "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": tflops / peak, "traffic": load_traffic(w.name) if args.out_dtype == "same" else None,
         },
         "secondary": sec,
         "cpu_baseline": cpu,

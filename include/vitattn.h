@@ -34,11 +34,20 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v and o (all four share it). */
+/*
+ * Element types of q, k, v and o.  The 16-bit kinds multiply in their own
+ * precision with float32 accumulation: the softmax weights are rounded to the
+ * input kind (nearest even) before the P.V product, and a 16-bit output is
+ * rounded to nearest even.  F16 and the float32 outputs follow "hf2q
+ * src/inference/vision/vit_gpu.rs", vit_attention_gpu (the peer-precision
+ * attention: K and V staged in F16 with float32 accumulation, F32 outputs).
+ */
 typedef enum {
-  VITATTN_DTYPE_F32 = 0,  /* IEEE float32; computed in float32 (float32 MFMA) */
-  VITATTN_DTYPE_BF16 = 1  /* bfloat16; bf16 MFMA products, float32 accumulation,
-                             output rounded to nearest even */
+  VITATTN_DTYPE_F32 = 0,          /* q, k, v, o float32; computed in float32 (float32 MFMA) */
+  VITATTN_DTYPE_BF16 = 1,         /* q, k, v, o bfloat16 */
+  VITATTN_DTYPE_F16 = 2,          /* q, k, v, o IEEE half */
+  VITATTN_DTYPE_BF16_OUT_F32 = 3, /* q, k, v bfloat16; o float32 (not rounded to 16 bits) */
+  VITATTN_DTYPE_F16_OUT_F32 = 4   /* q, k, v IEEE half; o float32 */
 } vitattn_dtype_t;
 
 /* Status codes.  Every entry point returns one of these. */
@@ -46,7 +55,7 @@ typedef enum {
   VITATTN_OK = 0,
   VITATTN_ERR_INVALID_ARG = -1,           /* null/misaligned pointer, bad count, non-finite scale */
   VITATTN_ERR_UNSUPPORTED_HEAD_DIM = -2,  /* head_dim not in {64, 72, 80, 128} */
-  VITATTN_ERR_UNSUPPORTED_DTYPE = -3,     /* dtype not a vitattn_dtype_t value */
+  VITATTN_ERR_UNSUPPORTED_DTYPE = -3,     /* dtype not a vitattn_dtype_t value (0 .. 4) */
   VITATTN_ERR_NO_DEVICE = -4,             /* no HIP device, or the current one is not gfx950 */
   VITATTN_ERR_OOM = -5,                   /* reserved: the forward pass allocates nothing */
   VITATTN_ERR_HIP = -6                    /* a HIP runtime call or kernel launch failed */
@@ -55,11 +64,13 @@ typedef enum {
 /*
  * vitattn_fwd -- enqueue one attention forward pass on `stream`.
  *
- * q, k, v : DEVICE pointers, contiguous [T, n_heads, head_dim] of `dtype`,
- *           T = cu_seqlens[n_seqs].  16-byte aligned.  Read only.
- * o       : DEVICE pointer, contiguous [T, n_heads, head_dim] of `dtype`,
- *           16-byte aligned, must not overlap q, k or v.  Every row that lies
- *           in some sequence is written; nothing else is.
+ * q, k, v : DEVICE pointers, contiguous [T, n_heads, head_dim] of the input
+ *           element type of `dtype`, T = cu_seqlens[n_seqs].  16-byte aligned.
+ *           Read only.
+ * o       : DEVICE pointer, contiguous [T, n_heads, head_dim] of the output
+ *           element type of `dtype`, 16-byte aligned, must not overlap q, k or
+ *           v.  Every row that lies in some sequence is written; nothing else
+ *           is.
  * cu_seqlens : DEVICE pointer to int32[n_seqs + 1]: cu_seqlens[0] is the
  *           first token row, the array is non-decreasing and sequence s owns
  *           rows [cu_seqlens[s], cu_seqlens[s+1]).  Zero-length sequences are

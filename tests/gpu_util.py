@@ -10,7 +10,11 @@ import oracle
 import vision_transformer_attention_amd as vta
 from vision_transformer_attention_amd import inputs
 
-TOL = {inputs.F32: 1e-4, inputs.BF16: 2e-2}
+# max-abs tolerances by input kind: float32 1e-4 and bfloat16 2e-2 (the stated targets); half
+# 1e-2: the weights rounded to half (relative 2^-11) move an output by at most
+# 2^-11 * 2 max|v| ~ 5e-3 for N(0,1) values, and a half output adds a rounding of ~2.4e-3.
+# A float32 output keeps the tolerance of its input kind.
+TOL = {inputs.F32: 1e-4, inputs.BF16: 2e-2, inputs.F16: 1e-2}
 DEV = "cuda:0"
 
 
@@ -19,14 +23,14 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(q, k, v, cu, scale, stream=None):
+def run_gpu(q, k, v, cu, scale, stream=None, out_dtype=None):
     d = torch.device(DEV)
     qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
     if stream is None:
-        o = vta.fwd(qd, kd, vd, cud, scale)
+        o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype)
     else:
         with torch.cuda.stream(stream):
-            o = vta.fwd(qd, kd, vd, cud, scale)
+            o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype)
         stream.synchronize()
     torch.cuda.synchronize()
     return o.cpu()
@@ -62,11 +66,13 @@ def sample_rows(cu: np.ndarray, bm: int = 128, extra: int = 6, seed: int = 0) ->
     return np.array(sorted(rows), np.int64)
 
 
-def check_workload(w: inputs.Workload, full: bool, rows=None):
+def check_workload(w: inputs.Workload, full: bool, rows=None, out_dtype=None):
     say(f"[parity] {w.name}: lengths={list(w.lengths)[:10]}{'...' if len(w.lengths) > 10 else ''} "
-        f"H={w.n_heads} Hkv={w.kv_heads} D={w.head_dim} {w.dtype} seed={w.seed} full={full}")
+        f"H={w.n_heads} Hkv={w.kv_heads} D={w.head_dim} {w.dtype} out={out_dtype} seed={w.seed} full={full}")
     q, k, v, cu, scale = inputs.make(w)
-    o = run_gpu(q, k, v, cu, scale)
+    o = run_gpu(q, k, v, cu, scale, out_dtype=out_dtype)
+    if out_dtype is not None:
+        assert o.dtype == out_dtype
     assert torch.isfinite(o.float()).all()
     if full:
         ref = oracle.attention(q, k, v, cu, scale)

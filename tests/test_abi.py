@@ -62,8 +62,12 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     (dict(n_heads=-3), INVALID),
     (dict(head_dim=96), BAD_HD),
     (dict(head_dim=0), BAD_HD),
-    (dict(dtype=2), BAD_DT),
+    (dict(dtype=5), BAD_DT),
     (dict(dtype=-1), BAD_DT),
+    (dict(dtype=2, head_dim=96), BAD_HD),   # f16: a known dtype, so the head_dim is what fails
+    (dict(dtype=3, head_dim=96), BAD_HD),   # bf16 in, f32 out
+    (dict(dtype=4, head_dim=96), BAD_HD),   # f16 in, f32 out
+    (dict(dtype=4, n_seqs=0), OK),
     (dict(scale=float("nan")), INVALID),
     (dict(scale=float("inf")), INVALID),
     (dict(q=0), INVALID),
@@ -108,6 +112,7 @@ def test_kernel_config_validates(lib):
     x = ctypes.c_int32(0)
     assert lib.vitattn_kernel_config(96, 1, ctypes.byref(x), None, None, None) == BAD_HD
     assert lib.vitattn_kernel_config(80, 5, None, None, None, None) == BAD_DT
+    assert lib.vitattn_kernel_config(72, 4, None, None, None, None) != BAD_DT
 
 
 def _gpu_present():
@@ -140,3 +145,16 @@ def test_binding_rejects_cpu_and_bad_tensors():
         vta.fwd(q, q, q, cu)  # CPU tensors: the library never computes on the CPU
     with pytest.raises(TypeError):
         vta.fwd(q.float().numpy(), q, q, cu)
+
+
+def test_binding_dtype_codes():
+    import torch
+    from vision_transformer_attention_amd import binding as b
+    assert b._call_code(torch.float32, torch.float32) == 0
+    assert b._call_code(torch.bfloat16, torch.bfloat16) == 1
+    assert b._call_code(torch.float16, torch.float16) == 2
+    assert b._call_code(torch.bfloat16, torch.float32) == 3
+    assert b._call_code(torch.float16, torch.float32) == 4
+    for bad in ((torch.float32, torch.bfloat16), (torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16)):
+        with pytest.raises(TypeError):
+            b._call_code(*bad)

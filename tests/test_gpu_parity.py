@@ -1,6 +1,7 @@
 """HIP path vs the float64 oracle, element by element, through the C ABI.
 
-Tolerances: max-abs 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs.
+Tolerances: max-abs 1e-4 for float32 inputs, 2e-2 for bfloat16 and 1e-2 for half inputs
+(``gpu_util.TOL`` derives the last).
 The small workloads are compared in full; the packed batch and the long
 sequence (full size, same launch as the benchmark) on sampled rows that cover
 every image's first and last rows and tile boundaries, plus properties that hold
@@ -177,3 +178,41 @@ def test_grouped_query_equals_repeated_kv_bitwise(dtype):
     o_mha = run_gpu(q, k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous(), cu,
                     scale)
     assert torch.equal(o_gqa, o_mha)
+
+
+# ---- half inputs, and float32 outputs from 16-bit inputs ----
+
+@pytest.mark.parametrize("head_dim", [64, 72, 80, 128])
+def test_half_edge_lengths(head_dim):
+    lengths = [1, 2, 31, 32, 33, 63, 64, 65, 127, 129, 300]
+    w = inputs.custom(lengths, n_heads=3, head_dim=head_dim, dtype=inputs.F16, seed=300 + head_dim)
+    check_workload(w, full=True)
+
+
+@pytest.mark.parametrize("head_dim", [80, 128])
+def test_half_rising_and_jumping_scores(head_dim):
+    # half keeps its weights in [2^-14 .., 2^15): the raise path runs whenever a score climbs
+    # 15 log2 units past the offset, many times over these ramps and spikes
+    w = inputs.custom([1000, 777, 64, 33, 5], n_heads=2, head_dim=head_dim, dtype=inputs.F16, seed=31,
+                      key_ramp=300.0, spikes=2)
+    check_workload(w, full=True)
+
+
+def test_half_page_912():
+    w = inputs.custom([912], n_heads=16, head_dim=80, dtype=inputs.F16, seed=32, token_factor=(0.5, 2.0))
+    check_workload(w, full=True)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [(inputs.BF16, 80), (inputs.BF16, 128), (inputs.F16, 64),
+                                             (inputs.F16, 72)])
+def test_float32_output_from_16_bit_inputs(dtype, head_dim):
+    w = inputs.custom([1, 65, 300, 129], n_heads=3, head_dim=head_dim, dtype=dtype, seed=33 + head_dim)
+    o32, _ = check_workload(w, full=True, out_dtype=torch.float32)
+    # the 16-bit output is the float32 one rounded to nearest even, bit for bit
+    q, k, v, cu, scale = inputs.make(w)
+    o16 = run_gpu(q, k, v, cu, scale)
+    assert torch.equal(o32.to(o16.dtype), o16)
+
+
+def test_float32_output_grouped_query_packed_sampled():
+    check_workload(inputs.WORKLOADS["packed-varlen-8-gqa4"], full=False, out_dtype=torch.float32)

@@ -16,6 +16,9 @@ _LIB_NAME = "libvitattn.so"
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
+DTYPE_BF16_OUT_F32 = 3
+DTYPE_F16_OUT_F32 = 4
 HEAD_DIMS = (64, 72, 80, 128)
 
 _lib = None
@@ -70,9 +73,21 @@ def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
+    if t.dtype == torch.float16:
+        return DTYPE_F16
     if t.dtype == torch.float32:
         return DTYPE_F32
-    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+    raise TypeError(f"q/k/v must be bfloat16, float16 or float32, got {t.dtype}")
+
+
+def _call_code(in_dtype, out_dtype) -> int:
+    """The vitattn_dtype_t code for inputs of in_dtype written as out_dtype."""
+    import torch
+    if out_dtype == in_dtype:
+        return {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}[in_dtype]
+    if out_dtype == torch.float32 and in_dtype in (torch.bfloat16, torch.float16):
+        return DTYPE_BF16_OUT_F32 if in_dtype == torch.bfloat16 else DTYPE_F16_OUT_F32
+    raise TypeError(f"no kernel writes {out_dtype} from {in_dtype} inputs (16-bit inputs may write float32)")
 
 
 def check_cu_seqlens(cu_host, total_tokens: int) -> None:
@@ -93,7 +108,7 @@ def kernel_config(head_dim: int, dtype) -> dict:
     """The launch ``vitattn_fwd`` makes for (head_dim, dtype) on the current device."""
     import torch
     lib = load_library()
-    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32 if dtype == torch.float32 else -1
+    code = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32, torch.float16: DTYPE_F16}.get(dtype, -1)
     vals = [ctypes.c_int32(0) for _ in range(4)]
     _check(lib, lib.vitattn_kernel_config(head_dim, code, *[ctypes.byref(x) for x in vals]))
     return dict(zip(("block_m", "block_n", "waves", "grid"), (x.value for x in vals)))
@@ -115,7 +130,7 @@ def fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_s
                                     ctypes.c_float(scale), dtype_code, stream))
 
 
-def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True):
+def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True, out_dtype=None):
     """Bidirectional attention over packed sequences; returns ``o`` like ``q``.
 
     q: contiguous CUDA (HIP) tensor ``[T, H, D]`` of bfloat16 or float32, D in
@@ -124,7 +139,8 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
     ``h // (H // Hkv)``).  cu_seqlens: int32 ``[n_seqs + 1]`` prefix array on the
     same device (a CPU copy is checked on the host when ``check_cu``).  scale
     defaults to ``1/sqrt(D)``; any finite value (1.0 included) is passed through
-    unchanged.
+    unchanged.  The output has q's dtype, or ``out_dtype`` (or ``out``'s dtype):
+    bfloat16 and float16 inputs may be written as float32.
     """
     import torch
     lib = load_library()
@@ -145,7 +161,10 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
         raise TypeError("q, k and v must have the same dtype")
     if q.device != k.device or q.device != v.device:
         raise ValueError("q, k and v must be on the same device")
-    code = _dtype_code(q)
+    _dtype_code(q)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
+    code = _call_code(q.dtype, out_dtype)
     t_tokens, n_heads, head_dim = q.shape
     if head_dim not in HEAD_DIMS:
         raise ValueError(f"head_dim {head_dim} not in {HEAD_DIMS}")
@@ -161,9 +180,9 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
     if not math.isfinite(scale):
         raise ValueError("scale must be finite")
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and device and the output dtype")
     n_seqs = cu_dev.numel() - 1
     if t_tokens == 0 or n_seqs == 0:
         return out

@@ -461,10 +461,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 // Both are filled by buffer_load_dwordx4 with the lds bit: lane l of a wave-wide load
 // lands at base + 16*l, so each wave-wide load fills 64 consecutive chunk slots.
 // ---------------------------------------------------------------------------
-template <int D_, int QB_, int NW_, int BN_>
+// E_: element kind of q, k, v (kBF16 or kF16); OF32_: the output is float32 instead of the
+// input element type.
+constexpr int kBF16 = 0, kF16 = 1;
+template <int D_, int QB_, int NW_, int BN_, int E_ = kBF16, bool OF32_ = false>
 struct Bf16Cfg {
-  using elem_t = __bf16;
-  static constexpr int D = D_, QB = QB_, NW = NW_, BN = BN_;
+  using elem_t = __bf16;  // 16-bit storage; the bits are bf16 or f16 by E
+  static constexpr int D = D_, QB = QB_, NW = NW_, BN = BN_, E = E_;
+  static constexpr bool OF32 = OF32_;
   static constexpr int NT = NW * 64;
   static constexpr int NQ = QB * 16;            // queries per wavefront
   static constexpr int BM = NW * NQ;            // queries per work item
@@ -576,6 +580,47 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// The two 16-bit element kinds.  Operands travel as raw 16-bit lanes (bf16x8_t, s16x4_t)
+// and are reinterpreted for the f16 instructions.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// D += A.B, 16x16x32 (A, B: 8 elements per lane)
+template <int E>
+__device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  if constexpr (E == kBF16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+// D = A.B, 16x16x16 on a zero accumulator (A, B: 4 elements per lane)
+template <int E>
+__device__ __forceinline__ f32x4_t mma16_zero(s16x4_t a, s16x4_t b) {
+  if constexpr (E == kBF16) return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b),
+                                                 f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+// two floats rounded to nearest even, packed
+template <int E>
+__device__ __forceinline__ unsigned cvt_pk(float a, float b) {
+  if constexpr (E == kBF16) return cvt_pk_bf16(a, b);
+  else return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+// 1.0 twice, in the element kind
+template <int E>
+constexpr unsigned kOnes2 = E == kBF16 ? 0x3f803f80u : 0x3c003c00u;
+// The exponent window of the weights.  bf16 has float32's exponent range: the offset sits
+// kHeadroom (16) above the reference max and is raised once a weight would reach 2.  f16
+// has 5 exponent bits (normal numbers 2^-14 .. 65504): the offset is the reference max
+// itself and is raised once a weight would reach 2^15, so weights stay normal-range
+// (the largest at least 1) and never overflow.
+template <int E>
+constexpr float kHead = E == kBF16 ? kHeadroom : 0.0f;
+template <int E>
+constexpr float kRaise = E == kBF16 ? 1.0f : 15.0f;
+
 // Operand fragments of one 32-key compute step, read from the LDS tile.
 //   K (A operand of S^T = K.Q^T): lane (c, g) holds key kb0+kb*16+c, dims ks*32+8g..+8,
 //     and for the 16-deep tail dims NK32*32+4g..+4.
@@ -634,7 +679,7 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
-        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(K.t[kb], QT[qb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        S[kb][qb] = mma16_zero<C::E>(K.t[kb], QT[qb]);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
@@ -650,7 +695,7 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
-        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K.a[kb][ks], Q[qb][ks], S[kb][qb], 0, 0, 0);
+        S[kb][qb] = mma32<C::E>(K.a[kb][ks], Q[qb][ks], S[kb][qb]);
 }
 
 // Softmax weights and O^T += V^T.P^T for one 32-key step.
@@ -686,7 +731,7 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
       float mx = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
                        fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
       mx = max_4groups(mx);  // finite: at least one key of the step is in the sequence
-      negM[qb] = -__builtin_fmaf(mx, c2, kHeadroom);
+      negM[qb] = -__builtin_fmaf(mx, c2, kHead<C::E>);
     }
   }
   // t = c2*s - M, in place
@@ -709,14 +754,14 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
       for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) hi = fmaxf(hi, S[kb][qb][r]);
-    if (__builtin_expect(__any(hi >= 1.0f), 0)) {  // rare: some row max rose by more than kHeadroom + 1
+    if (__builtin_expect(__any(hi >= kRaise<C::E>), 0)) {  // rare: some row max rose past the window
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
         float tm = fmaxf(fmaxf(fmaxf(S[0][qb][0], S[0][qb][1]), fmaxf(S[0][qb][2], S[0][qb][3])),
                          fmaxf(fmaxf(S[1][qb][0], S[1][qb][1]), fmaxf(S[1][qb][2], S[1][qb][3])));
         tm = max_4groups(tm);
-        if (tm >= 1.0f) {  // the same decision in all four lanes of the row
-          const float delta = tm + kHeadroom;
+        if (tm >= kRaise<C::E>) {  // the same decision in all four lanes of the row
+          const float delta = tm + kHead<C::E>;
           negM[qb] -= delta;
           const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
@@ -740,7 +785,7 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
   for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      W[qb][j] = cvt_pk_bf16(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
+      W[qb][j] = cvt_pk<C::E>(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
                              __builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2 + 1]));
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
@@ -749,13 +794,12 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
-      O[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb], 0, 0, 0);
+      O[db][qb] = mma32<C::E>(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb]);
   // row sums of the rounded weights, by an MFMA against a block of ones
-  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const u32x4_t ones = {kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>};
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb)
-    O[C::NDB][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ones),
-                                                             __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb], 0, 0, 0);
+    O[C::NDB][qb] = mma32<C::E>(__builtin_bit_cast(bf16x8_t, ones), __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb]);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
@@ -810,7 +854,7 @@ __device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, co
 // are masked in the first step, and every later step is a full one.
 template <class C>
 __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                         const __bf16* __restrict__ v, __bf16* __restrict__ o, int n_heads,
+                                         const __bf16* __restrict__ v, void* __restrict__ o, int n_heads,
                                          int n_kv_heads, int kv_group, float c2, int negate, lds_u8_t* stage,
                                          unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave,
                                          int lane) {
@@ -901,8 +945,12 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
         const int d0 = db * 16 + 4 * g;
         if (d0 < C::D) {
           const f32x4_t x = O[db][qb];
-          *reinterpret_cast<u32x2_t*>(o + ((size_t)row * n_heads + item.head) * C::D + d0) =
-              u32x2_t{cvt_pk_bf16(x[0] * inv, x[1] * inv), cvt_pk_bf16(x[2] * inv, x[3] * inv)};
+          const size_t at = ((size_t)row * n_heads + item.head) * C::D + d0;
+          if constexpr (C::OF32)
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + at) = x * inv;
+          else
+            *reinterpret_cast<u32x2_t*>(static_cast<__bf16*>(o) + at) =
+                u32x2_t{cvt_pk<C::E>(x[0] * inv, x[1] * inv), cvt_pk<C::E>(x[2] * inv, x[3] * inv)};
         }
       }
     }
@@ -916,10 +964,11 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
 template <class CA, class CB>
 __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2,
+    void* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2,
     int negate) {
-  static_assert(CA::D == CB::D && CA::NW == CB::NW && CA::BN == CB::BN && CA::STAGE_BYTES == CB::STAGE_BYTES,
-                "the two query-block sizes share the staging layout");
+  static_assert(CA::D == CB::D && CA::NW == CB::NW && CA::BN == CB::BN && CA::STAGE_BYTES == CB::STAGE_BYTES &&
+                    CA::E == CB::E && CA::OF32 == CB::OF32,
+                "the two query-block sizes share the staging layout and the element kinds");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
   lds_u8_t* stage = (lds_u8_t*)smem + ((sizeof(PlanLds) + 15) / 16) * 16;
@@ -1021,19 +1070,17 @@ KernelDesc describe_bf16() {
 #ifndef VITATTN_BF16_QB_SMALL
 #define VITATTN_BF16_QB_SMALL 1
 #endif
-using K_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
-using K_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
-using K_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB, VITATTN_BF16_NW, 64>;
-using K_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_128, VITATTN_BF16_NW, 64>;
-using S_bf16_64 = Bf16Cfg<64, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
-using S_bf16_72 = Bf16Cfg<72, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
-using S_bf16_80 = Bf16Cfg<80, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
-using S_bf16_128 = Bf16Cfg<128, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64>;
+// 16-bit kernels: the large and the small query blocks for each element and output kind
+template <int D, int E, bool OF32>
+using KCfg = Bf16Cfg<D, D == 128 ? VITATTN_BF16_QB_128 : VITATTN_BF16_QB, VITATTN_BF16_NW, 64, E, OF32>;
+template <int D, int E, bool OF32>
+using SCfg = Bf16Cfg<D, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, E, OF32>;
 using K_f32_64 = F32Traits<64, 1, 4, 32>;
 using K_f32_72 = F32Traits<72, 1, 4, 32>;
 using K_f32_80 = F32Traits<80, 1, 4, 32>;
 using K_f32_128 = F32Traits<128, 1, 4, 32>;
 
+// Kernel table index: dtype * 4 + head_dim slot (dtype codes as in vitattn_dtype_t).
 int kernel_index(int32_t head_dim, int32_t dtype) {
   int hd;
   switch (head_dim) {
@@ -1046,20 +1093,34 @@ int kernel_index(int32_t head_dim, int32_t dtype) {
   return dtype * 4 + hd;
 }
 
-KernelDesc kernel_desc(int idx) {
-  switch (idx) {
-    case 0: return describe_f32<K_f32_64>();
-    case 1: return describe_f32<K_f32_72>();
-    case 2: return describe_f32<K_f32_80>();
-    case 3: return describe_f32<K_f32_128>();
-    case 4: return describe_bf16<K_bf16_64, S_bf16_64>();
-    case 5: return describe_bf16<K_bf16_72, S_bf16_72>();
-    case 6: return describe_bf16<K_bf16_80, S_bf16_80>();
-    default: return describe_bf16<K_bf16_128, S_bf16_128>();
+template <int E, bool OF32>
+KernelDesc describe16(int hd) {
+  switch (hd) {
+    case 0: return describe_bf16<KCfg<64, E, OF32>, SCfg<64, E, OF32>>();
+    case 1: return describe_bf16<KCfg<72, E, OF32>, SCfg<72, E, OF32>>();
+    case 2: return describe_bf16<KCfg<80, E, OF32>, SCfg<80, E, OF32>>();
+    default: return describe_bf16<KCfg<128, E, OF32>, SCfg<128, E, OF32>>();
   }
 }
 
-constexpr int kNumKernels = 8;
+KernelDesc kernel_desc(int idx) {
+  const int hd = idx % 4;
+  switch (idx / 4) {
+    case VITATTN_DTYPE_F32:
+      switch (hd) {
+        case 0: return describe_f32<K_f32_64>();
+        case 1: return describe_f32<K_f32_72>();
+        case 2: return describe_f32<K_f32_80>();
+        default: return describe_f32<K_f32_128>();
+      }
+    case VITATTN_DTYPE_BF16: return describe16<kBF16, false>(hd);
+    case VITATTN_DTYPE_F16: return describe16<kF16, false>(hd);
+    case VITATTN_DTYPE_BF16_OUT_F32: return describe16<kBF16, true>(hd);
+    default: return describe16<kF16, true>(hd);
+  }
+}
+
+constexpr int kNumKernels = 20;  // 5 dtype codes x 4 head dims
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
@@ -1119,8 +1180,8 @@ int get_device_state(DeviceState** out) {
 }
 
 int validate(int32_t head_dim, int32_t dtype) {
-  if (dtype != VITATTN_DTYPE_F32 && dtype != VITATTN_DTYPE_BF16)
-    return fail(VITATTN_ERR_UNSUPPORTED_DTYPE, "dtype %d is not VITATTN_DTYPE_F32 (0) or VITATTN_DTYPE_BF16 (1)", dtype);
+  if (dtype < VITATTN_DTYPE_F32 || dtype > VITATTN_DTYPE_F16_OUT_F32)
+    return fail(VITATTN_ERR_UNSUPPORTED_DTYPE, "dtype %d is not a vitattn_dtype_t code (0 .. 4)", dtype);
   if (kernel_index(head_dim, dtype) < 0)
     return fail(VITATTN_ERR_UNSUPPORTED_HEAD_DIM, "head_dim %d not in {64, 72, 80, 128}", head_dim);
   return VITATTN_OK;
@@ -1192,11 +1253,11 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   for (int32_t s0 = 0; s0 < n_seqs; s0 += kMaxSeqs) {
     const int n = n_seqs - s0 < kMaxSeqs ? n_seqs - s0 : kMaxSeqs;
-    if (dtype == VITATTN_DTYPE_BF16) {
+    if (dtype != VITATTN_DTYPE_F32) {  // 16-bit inputs (bf16 or f16 bits); o by the output kind
       const __bf16* qq = static_cast<const __bf16*>(q);
       const __bf16* kk = static_cast<const __bf16*>(k);
       const __bf16* vv = static_cast<const __bf16*>(v);
-      __bf16* oo = static_cast<__bf16*>(o);
+      void* oo = o;
       const int32_t* cc = cu_seqlens + s0;
       void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&n_kv_heads,
                       (void*)&c2, (void*)&negate};

@@ -8,7 +8,7 @@ Recipe (every workload): ``numpy.random.default_rng(seed)`` (PCG64) draws float3
 ``standard_normal`` arrays in the fixed order Q, K, V, row-major ``[T, H, D]`` for Q
 and ``[T, Hkv, D]`` for K and V (seq-major tokens, then heads, then head_dim; Hkv = H
 except for grouped-query workloads), then any per-token factors.  bf16
-tensors are the float32 draws rounded to nearest-even by ``torch.Tensor.to``.
+and f16 tensors are the float32 draws rounded to nearest-even by ``torch.Tensor.to``.
 The sequence-length prefix array ``cu_seqlens`` is int32 ``[n_seqs + 1]``.
 
 The shapes follow the pages' vision-tower workloads: a 196-patch image at hidden
@@ -26,6 +26,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -76,6 +77,8 @@ WORKLOADS: dict[str, Workload] = {
     "long-16384": Workload("long-16384", (16384,), 16, 128, BF16, seed=5),
     # grouped-query attention: the packed batch with 4 K/V heads for the 16 query heads
     "packed-varlen-8-gqa4": Workload("packed-varlen-8-gqa4", PACKED_LENGTHS, 16, 80, BF16, seed=6, n_kv_heads=4),
+    # the packed batch in half precision
+    "packed-varlen-8-f16": Workload("packed-varlen-8-f16", PACKED_LENGTHS, 16, 80, F16, seed=7),
 }
 
 
@@ -130,7 +133,7 @@ def make(w: Workload | str):
     if isinstance(w, str):
         w = WORKLOADS[w]
     q, k, v = draw_f32(w)
-    tdt = torch.float32 if w.dtype == F32 else torch.bfloat16
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[w.dtype]
     qt, kt, vt = (torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
     cu = torch.from_numpy(w.cu_seqlens())
     return qt, kt, vt, cu, w.softmax_scale

@@ -21,6 +21,11 @@ the same sequence only.  Sources, by page title:
   ``vit_repeat_kv_gpu`` doc and its use in ``gemma4v_block_forward_gpu`` (grouped-query
   attention: K and V carry fewer heads, and query head ``h`` reads K/V head
   ``h // num_kv_groups``).
+* "hanzo-ml 0.11.4 src/vulkan_backend.rs" -- ``flash_attn_gpu`` doc (aligned causal
+  masking: query ``qi`` sees keys ``kj <= qi + (Lk - Lq)``; inside one image
+  ``Lk = Lq``, so ``kj <= qi``).  The key window of the encoder attention meta
+  ("inferencelayer 0.2.1 src/vision_gpu.rs", ``VisionGpu::forward_one``: window 0
+  is unrestricted) is read as ``|qi - kj| < window``.
 
 Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
 hand-derived golden values, invariants, and a library routine (PyTorch's CPU
@@ -67,6 +72,14 @@ def _bind(lib):
     lib.vitattn_ref_rows_gqa_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_double, i64p, ctypes.c_int64]
     lib.vitattn_ref_rows_gqa_f64.restype = ctypes.c_int
+    lib.vitattn_ref_fwd_masked_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_int32,
+                                               ctypes.c_int32]
+    lib.vitattn_ref_fwd_masked_f64.restype = ctypes.c_int
+    lib.vitattn_ref_rows_masked_f64.argtypes = [f32p, f32p, f32p, f64p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_int32,
+                                                ctypes.c_int32, i64p, ctypes.c_int64]
+    lib.vitattn_ref_rows_masked_f64.restype = ctypes.c_int
     lib.vitattn_ref_row_probs_f64.argtypes = [f32p, f32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_double, ctypes.c_int64, ctypes.c_int32, f64p]
     lib.vitattn_ref_row_probs_f64.restype = ctypes.c_int64
@@ -125,11 +138,20 @@ def _heads(q, k, v):
     return t, h, k.shape[1], d
 
 
-def attention(q, k, v, cu_seqlens, scale: float, lib=None) -> np.ndarray:
+def _mask(causal, window) -> tuple[int, int]:
+    if causal not in (False, True, 0, 1) or int(window) < 0:
+        raise ValueError("causal must be 0/1 and window >= 0")
+    return int(bool(causal)), int(window)
+
+
+def attention(q, k, v, cu_seqlens, scale: float, lib=None, causal=False, window: int = 0) -> np.ndarray:
     """Full float64 output ``[T, H, D]``; rows outside every sequence stay 0.
 
     k and v may have fewer heads than q (grouped-query attention): query head h
-    uses K/V head h // (H // Hkv)."""
+    uses K/V head h // (H // Hkv).  ``causal`` keeps, inside each sequence, the
+    keys at or before the query; ``window`` > 0 keeps the keys less than
+    ``window`` positions from it (0: all)."""
+    cz, wd = _mask(causal, window)
     lib = lib or load()
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     cu = _cu(cu_seqlens)
@@ -137,16 +159,18 @@ def attention(q, k, v, cu_seqlens, scale: float, lib=None) -> np.ndarray:
     if len(cu) < 1 or cu[0] != 0 or cu[-1] != t or np.any(np.diff(cu) < 0):
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     o = np.zeros((t, h, d), dtype=np.float64)
-    rc = lib.vitattn_ref_fwd_gqa_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
-                                     _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d,
-                                     float(scale))
+    rc = lib.vitattn_ref_fwd_masked_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                        _ptr(v, ctypes.c_float), _ptr(o, ctypes.c_double),
+                                        _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d, float(scale), cz, wd)
     if rc != 0:
         raise RuntimeError("oracle failed")
     return o
 
 
-def attention_rows(q, k, v, cu_seqlens, scale: float, rows, lib=None) -> np.ndarray:
-    """Float64 output for the token rows listed in ``rows`` only: ``[len(rows), H, D]``."""
+def attention_rows(q, k, v, cu_seqlens, scale: float, rows, lib=None, causal=False, window: int = 0) -> np.ndarray:
+    """Float64 output for the token rows listed in ``rows`` only: ``[len(rows), H, D]``
+    (masks as in ``attention``)."""
+    cz, wd = _mask(causal, window)
     lib = lib or load()
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     cu = _cu(cu_seqlens)
@@ -155,9 +179,10 @@ def attention_rows(q, k, v, cu_seqlens, scale: float, rows, lib=None) -> np.ndar
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     r = np.ascontiguousarray(np.asarray(rows), dtype=np.int64)
     o = np.zeros((len(r), h, d), dtype=np.float64)
-    rc = lib.vitattn_ref_rows_gqa_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
-                                      _ptr(o, ctypes.c_double), _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d,
-                                      float(scale), _ptr(r, ctypes.c_int64), len(r))
+    rc = lib.vitattn_ref_rows_masked_f64(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                         _ptr(v, ctypes.c_float), _ptr(o, ctypes.c_double),
+                                         _ptr(cu, ctypes.c_int32), len(cu) - 1, h, hkv, d, float(scale), cz, wd,
+                                         _ptr(r, ctypes.c_int64), len(r))
     if rc != 0:
         raise RuntimeError("oracle failed (bad rows?)")
     return o

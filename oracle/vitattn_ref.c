@@ -33,6 +33,20 @@
  *    vit_attention_scores_gpu: the scale is the caller's value (1/sqrt(hd) for
  *    a standard ViT, 1.0 for Gemma 4V), with no implicit scaling.
  *
+ * Masks (the *_masked_* entry points; causal = 0 and window = 0 is the
+ * definition above).  Within a sequence of length L, query position qi = i - a
+ * and key position kj = j - a, key j takes part in row i only if
+ *   - causal: kj <= qi + (Lk - Lq), the aligned causal rule of "hanzo-ml
+ *     0.11.4 src/vulkan_backend.rs", doc of flash_attn_gpu; here Lk = Lq = L
+ *     (self-attention inside one image), so kj <= qi;
+ *   - window > 0: |qi - kj| < window.  The pages name the window parameter of
+ *     the encoder attention ("inferencelayer 0.2.1 src/vision_gpu.rs",
+ *     VisionGpu::forward_one, the attention meta: window 0 means unrestricted)
+ *     without defining it; the reading taken here is a symmetric band of
+ *     half-width window - 1, which with causal = 1 is the last `window` keys up
+ *     to and including the query itself.
+ * Every row keeps at least itself (kj = qi passes both rules), so Z > 0.
+ *
  * Readings taken where the pages are silent: the max is subtracted before the
  * exponential (a two-pass softmax; mathematically the same result); the scale
  * multiplies the dot product before the max; inputs arrive as float32 values
@@ -49,23 +63,35 @@
 #include <omp.h>
 #endif
 
+/* Whether key j takes part in query row i of the sequence [a, b) (the mask
+ * rules in the header; causal = 0 and window = 0 keep every key). */
+static int ref_visible(int64_t a, int64_t b, int64_t i, int64_t j, int32_t causal, int32_t window) {
+  const int64_t qi = i - a, kj = j - a;
+  const int64_t lq = b - a, lk = b - a; /* self-attention: as many keys as queries */
+  if (causal && kj > qi + (lk - lq)) return 0;
+  if (window > 0 && (qi - kj >= window || kj - qi >= window)) return 0;
+  return 1;
+}
+
 /* One query row of one head: writes D outputs to out[0..D).  `w` is caller
  * scratch of at least (b - a) doubles.  K and V have n_kv_heads heads (a
  * divisor of n_heads); query head h reads K/V head h / (n_heads / n_kv_heads),
  * the grouping of "hf2q src/inference/vision/vit_gpu.rs", doc of
  * vit_repeat_kv_gpu (each K/V head serves num_kv_groups consecutive query
- * heads).  n_kv_heads == n_heads is plain multi-head attention. */
+ * heads).  n_kv_heads == n_heads is plain multi-head attention.  Keys that the
+ * mask rules exclude get weight exactly 0: they enter neither the max nor Z. */
 static void ref_one_row(const float* q, const float* k, const float* v,
                         int64_t a, int64_t b, int64_t i, int32_t h,
                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, double scale,
-                        double* w, double* out) {
+                        int32_t causal, int32_t window, double* w, double* out) {
   const int64_t row_stride = (int64_t)n_heads * head_dim;
   const int64_t kv_stride = (int64_t)n_kv_heads * head_dim;
   const int32_t hk = h / (n_heads / n_kv_heads);
   const float* qi = q + i * row_stride + (int64_t)h * head_dim;
-  /* pass 1: logits and their maximum */
+  /* pass 1: logits of the visible keys and their maximum */
   double m = -INFINITY;
   for (int64_t j = a; j < b; ++j) {
+    if (!ref_visible(a, b, i, j, causal, window)) continue;
     const float* kj = k + j * kv_stride + (int64_t)hk * head_dim;
     double dot = 0.0;
     for (int32_t d = 0; d < head_dim; ++d) dot += (double)qi[d] * (double)kj[d];
@@ -76,12 +102,13 @@ static void ref_one_row(const float* q, const float* k, const float* v,
   /* pass 2: weights, their sum, and the weighted average of V */
   double z = 0.0;
   for (int64_t j = a; j < b; ++j) {
-    double wj = exp(w[j - a] - m);
+    double wj = ref_visible(a, b, i, j, causal, window) ? exp(w[j - a] - m) : 0.0;
     w[j - a] = wj;
     z += wj;
   }
   for (int32_t e = 0; e < head_dim; ++e) out[e] = 0.0;
   for (int64_t j = a; j < b; ++j) {
+    if (w[j - a] == 0.0) continue;
     const float* vj = v + j * kv_stride + (int64_t)hk * head_dim;
     for (int32_t e = 0; e < head_dim; ++e) out[e] += w[j - a] * (double)vj[e];
   }
@@ -98,12 +125,14 @@ int vitattn_ref_threads(void) {
 }
 
 /* Full output o[T, H, D] (float64) for q [T, H, D] and k, v [T, Hkv, D]
- * (float32 values), Hkv a divisor of H.  Returns 0, or -1 on a bad argument or
- * an allocation failure. */
-int vitattn_ref_fwd_gqa_f64(const float* q, const float* k, const float* v, double* o,
-                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
-                            int32_t n_kv_heads, int32_t head_dim, double scale) {
+ * (float32 values), Hkv a divisor of H, under the mask rules (causal 0 or 1,
+ * window >= 0).  Returns 0, or -1 on a bad argument or an allocation failure. */
+int vitattn_ref_fwd_masked_f64(const float* q, const float* k, const float* v, double* o,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim, double scale,
+                               int32_t causal, int32_t window) {
   if (n_seqs < 0 || n_heads <= 0 || head_dim <= 0) return -1;
+  if ((causal != 0 && causal != 1) || window < 0) return -1;
   if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return -1;
   if (n_seqs == 0) return 0;
   if (!q || !k || !v || !o || !cu_seqlens) return -1;
@@ -127,13 +156,20 @@ int vitattn_ref_fwd_gqa_f64(const float* q, const float* k, const float* v, doub
         int32_t s = (int32_t)(p / n_heads), h = (int32_t)(p % n_heads);
         int64_t a = cu_seqlens[s], b = cu_seqlens[s + 1];
         for (int64_t i = a; i < b; ++i)
-          ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, w,
+          ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, causal, window, w,
                       o + (i * n_heads + h) * (int64_t)head_dim);
       }
       free(w);
     }
   }
   return failed ? -1 : 0;
+}
+
+/* No mask: every key of the sequence. */
+int vitattn_ref_fwd_gqa_f64(const float* q, const float* k, const float* v, double* o,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_dim, double scale) {
+  return vitattn_ref_fwd_masked_f64(q, k, v, o, cu_seqlens, n_seqs, n_heads, n_kv_heads, head_dim, scale, 0, 0);
 }
 
 /* Multi-head attention (as many K/V heads as query heads). */
@@ -145,12 +181,13 @@ int vitattn_ref_fwd_f64(const float* q, const float* k, const float* v, double* 
 
 /* Output for a chosen set of token rows only: o_rows[n_rows, H, D] (float64),
  * rows[r] a global token index in [0, T).  Used where the full output would
- * take too long.  Returns 0, or -1 on a bad argument. */
-int vitattn_ref_rows_gqa_f64(const float* q, const float* k, const float* v, double* o_rows,
-                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
-                             int32_t n_kv_heads, int32_t head_dim, double scale,
-                             const int64_t* rows, int64_t n_rows) {
+ * take too long, under the mask rules.  Returns 0, or -1 on a bad argument. */
+int vitattn_ref_rows_masked_f64(const float* q, const float* k, const float* v, double* o_rows,
+                                const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                                int32_t n_kv_heads, int32_t head_dim, double scale,
+                                int32_t causal, int32_t window, const int64_t* rows, int64_t n_rows) {
   if (n_seqs <= 0 || n_heads <= 0 || head_dim <= 0 || n_rows < 0) return -1;
+  if ((causal != 0 && causal != 1) || window < 0) return -1;
   if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return -1;
   if (!q || !k || !v || !o_rows || !cu_seqlens || (n_rows > 0 && !rows)) return -1;
   const int64_t total = cu_seqlens[n_seqs];
@@ -179,12 +216,20 @@ int vitattn_ref_rows_gqa_f64(const float* q, const float* k, const float* v, dou
         int32_t s = 0;
         while (!(cu_seqlens[s] <= i && i < cu_seqlens[s + 1])) ++s;
         ref_one_row(q, k, v, cu_seqlens[s], cu_seqlens[s + 1], i, h, n_heads, n_kv_heads,
-                    head_dim, scale, w, o_rows + (r * n_heads + h) * (int64_t)head_dim);
+                    head_dim, scale, causal, window, w, o_rows + (r * n_heads + h) * (int64_t)head_dim);
       }
       free(w);
     }
   }
   return failed ? -1 : 0;
+}
+
+int vitattn_ref_rows_gqa_f64(const float* q, const float* k, const float* v, double* o_rows,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                             int32_t n_kv_heads, int32_t head_dim, double scale,
+                             const int64_t* rows, int64_t n_rows) {
+  return vitattn_ref_rows_masked_f64(q, k, v, o_rows, cu_seqlens, n_seqs, n_heads, n_kv_heads, head_dim,
+                                     scale, 0, 0, rows, n_rows);
 }
 
 int vitattn_ref_rows_f64(const float* q, const float* k, const float* v, double* o_rows,

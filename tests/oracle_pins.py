@@ -248,10 +248,100 @@ def pin_gqa_constant_v_per_group(lib):
         assert np.allclose(got[:, h, :], h // 2 + 0.25, rtol=0, atol=1e-13)
 
 
+# ---- masks: aligned causal ("hanzo-ml 0.11.4 src/vulkan_backend.rs", flash_attn_gpu doc)
+# and a key window (the encoder attention meta of "inferencelayer 0.2.1 src/vision_gpu.rs",
+# window 0 = unrestricted; read as |qi - kj| < window)
+
+def pin_causal_torch_sdpa(lib):
+    # PyTorch's CPU SDPA in float64 with its own causal flag (for as many queries as keys
+    # it keeps key j <= query i), per image, also in its grouped-query mode
+    import torch
+    import torch.nn.functional as F
+    for h, hkv, seed in ((4, 4, 40), (8, 2, 41)):
+        q, k, v, cu = _rand_gqa([29, 1, 2, 64, 45], h, hkv, 12, seed=seed, std=1.4)
+        got = oracle.attention(q, k, v, cu, 0.33, lib=lib, causal=True)
+        for a, b in _segments(cu):
+            t = lambda x: torch.from_numpy(x[a:b].astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+            ref = F.scaled_dot_product_attention(t(q), t(k), t(v), scale=0.33, is_causal=True,
+                                                 enable_gqa=hkv != h)
+            ref = ref.squeeze(0).permute(1, 0, 2).numpy()
+            assert np.allclose(got[a:b], ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_causal_first_row_is_its_value(lib):
+    # the first token of an image sees only itself: its output is its own value row, exactly
+    q, k, v, cu = _rand([5, 1, 17], 3, 8, seed=42, std=2.0)
+    got = oracle.attention(q, k, v, cu, 0.9, lib=lib, causal=True)
+    for a, _ in _segments(cu):
+        assert np.array_equal(got[a], v[a].astype(np.float64))
+
+
+def pin_window_one_is_identity(lib):
+    # window 1 keeps only the key at the query's own position: O = V exactly, with or without causal
+    q, k, v, cu = _rand([9, 1, 33], 2, 8, seed=43, std=3.0)
+    for causal in (False, True):
+        got = oracle.attention(q, k, v, cu, 0.7, lib=lib, causal=causal, window=1)
+        assert np.array_equal(got, v.astype(np.float64))
+
+
+def _slice_attention(lib, q, k, v, i, lo, hi, scale):
+    """Unmasked attention of query row i over the keys [lo, hi) only, through the mask-free
+    oracle: one image of hi - lo rows whose queries are copies of row i and whose keys and
+    values are rows lo .. hi-1 (cut out with numpy)."""
+    n = hi - lo
+    qx = np.repeat(q[i:i + 1], n, axis=0)
+    return oracle.attention(qx, k[lo:hi], v[lo:hi], [0, n], scale, lib=lib)[0]
+
+
+def pin_causal_is_prefix_attention(lib):
+    # causal row i is bidirectional attention over the image's prefix [a, i]
+    q, k, v, cu = _rand([23, 40], 2, 10, seed=44, std=1.6)
+    got = oracle.attention(q, k, v, cu, 0.45, lib=lib, causal=True)
+    for a, b in _segments(cu):
+        for i in (a, a + 1, a + 7, b - 2, b - 1):
+            ref = _slice_attention(lib, q, k, v, i, a, i + 1, 0.45)
+            assert np.allclose(got[i], ref, rtol=1e-13, atol=1e-14)
+
+
+def pin_window_is_band_attention(lib):
+    # window W: row i is bidirectional attention over the keys [i-W+1, i+W) clipped to its
+    # image, and with causal over [i-W+1, i]
+    q, k, v, cu = _rand([37, 6, 50], 2, 8, seed=45, std=1.5)
+    for w in (2, 5, 16):
+        for causal in (False, True):
+            got = oracle.attention(q, k, v, cu, 0.5, lib=lib, causal=causal, window=w)
+            for a, b in _segments(cu):
+                for i in sorted({a, a + 1, a + 3, (a + b) // 2, b - 3, b - 1} & set(range(a, b))):
+                    lo, hi = max(a, i - w + 1), (i + 1 if causal else min(b, i + w))
+                    ref = _slice_attention(lib, q, k, v, i, lo, hi, 0.5)
+                    assert np.allclose(got[i], ref, rtol=1e-13, atol=1e-14), (w, causal, i)
+
+
+def pin_wide_window_is_no_window(lib):
+    # a window at least as long as every image changes nothing (the same sums, bit for bit)
+    q, k, v, cu = _rand([12, 30, 1], 2, 6, seed=46)
+    for causal in (False, True):
+        ref = oracle.attention(q, k, v, cu, 0.6, lib=lib, causal=causal)
+        for w in (30, 31, 1000):
+            assert np.array_equal(oracle.attention(q, k, v, cu, 0.6, lib=lib, causal=causal, window=w), ref)
+
+
+def pin_masked_rows_match_full(lib):
+    q, k, v, cu = _rand_gqa([12, 5, 30], 4, 2, 6, seed=47)
+    rows = np.array([0, 11, 12, 16, 17, 25, 46, 3], np.int64)
+    for causal, w in ((True, 0), (False, 4), (True, 7)):
+        full = oracle.attention(q, k, v, cu, 0.4, lib=lib, causal=causal, window=w)
+        got = oracle.attention_rows(q, k, v, cu, 0.4, rows, lib=lib, causal=causal, window=w)
+        assert np.array_equal(got, full[rows])
+
+
 PINS = [
     pin_golden, pin_scale_one_logistic, pin_single_key, pin_constant_v, pin_uniform_when_no_signal,
     pin_weights_are_a_distribution, pin_key_shift_invariance, pin_key_permutation_invariance,
     pin_affine_in_v, pin_convex_hull, pin_block_diagonal, pin_head_independence,
     pin_head_dim_zero_padding, pin_torch_sdpa, pin_rows_match_full,
     pin_gqa_is_repeated_kv, pin_gqa_torch_sdpa, pin_gqa_constant_v_per_group,
+    pin_causal_torch_sdpa, pin_causal_first_row_is_its_value, pin_window_one_is_identity,
+    pin_causal_is_prefix_attention, pin_window_is_band_attention, pin_wide_window_is_no_window,
+    pin_masked_rows_match_full,
 ]

@@ -33,13 +33,28 @@ MUTANTS = {
     "keys-cross-images": [
         ("double* w = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));",
          "double* w = (double*)malloc(sizeof(double) * (size_t)(cu_seqlens[n_seqs] + 1));"),
-        ("ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, w,\n                      o + (i * n_heads",
-         "ref_one_row(q, k, v, 0, cu_seqlens[n_seqs], i, h, n_heads, n_kv_heads, head_dim, scale, w,\n                      o + (i * n_heads"),
+        ("ref_one_row(q, k, v, a, b, i, h, n_heads, n_kv_heads, head_dim, scale, causal, window, w,",
+         "ref_one_row(q, k, v, 0, cu_seqlens[n_seqs], i, h, n_heads, n_kv_heads, head_dim, scale, causal, window, w,"),
     ],
-    "last-key-dropped": [("for (int64_t j = a; j < b; ++j) {\n    const float* kj",
-                          "for (int64_t j = a; j < b - 1; ++j) {\n    const float* kj")],
-    "max-subtracted-from-one-key": [("double wj = exp(w[j - a] - m);", "double wj = exp(w[j - a] - (j == a ? m : 0.0));")],
+    "last-key-dropped": [("for (int64_t j = a; j < b; ++j) {\n    if (!ref_visible",
+                          "for (int64_t j = a; j < b - 1; ++j) {\n    if (!ref_visible")],
+    "max-subtracted-from-one-key": [("exp(w[j - a] - m)", "exp(w[j - a] - (j == a ? m : 0.0))")],
     "sum-misses-first-key": [("    z += wj;\n", "    if (j > a) z += wj;\n")],
+    "causal-ignored": [("if (causal && kj > qi + (lk - lq)) return 0;", "if (0 && kj > qi + (lk - lq)) return 0;")],
+    "causal-flipped": [("if (causal && kj > qi + (lk - lq)) return 0;", "if (causal && kj < qi + (lk - lq)) return 0;")],
+    "causal-one-ahead": [("if (causal && kj > qi + (lk - lq)) return 0;",
+                          "if (causal && kj > qi + 1 + (lk - lq)) return 0;")],
+    "causal-drops-diagonal": [("if (causal && kj > qi + (lk - lq)) return 0;",
+                               "if (causal && kj >= qi + (lk - lq)) return 0;")],
+    "window-inclusive": [("if (window > 0 && (qi - kj >= window || kj - qi >= window)) return 0;",
+                          "if (window > 0 && (qi - kj > window || kj - qi > window)) return 0;")],
+    "window-one-sided": [("if (window > 0 && (qi - kj >= window || kj - qi >= window)) return 0;",
+                          "if (window > 0 && (qi - kj >= window)) return 0;")],
+    "window-ignored-with-causal": [("if (window > 0 && (qi - kj >= window",
+                                    "if (window > 0 && !causal && (qi - kj >= window")],
+    "window-ignored": [("if (window > 0 && (qi - kj >= window", "if (0 && (qi - kj >= window")],
+    "window-from-image-start": [("if (window > 0 && (qi - kj >= window || kj - qi >= window)) return 0;",
+                                 "if (window > 0 && (kj >= window)) return 0;")],
     "value-head-ignored": [("const float* vj = v + j * kv_stride + (int64_t)hk * head_dim;",
                             "const float* vj = v + j * kv_stride;")],
 }

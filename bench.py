@@ -32,7 +32,24 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False):
+def visible_pairs(lengths, causal: bool, window: int) -> int:
+    """(query, key) pairs a mask keeps, summed over the sequences (all L^2 without one)."""
+    import numpy as np
+    total = 0
+    for n in lengths:
+        i = np.arange(int(n), dtype=np.int64)
+        lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros_like(i)
+        hi = np.full_like(i, int(n) - 1)
+        if window > 0:
+            hi = np.minimum(hi, i + window - 1)
+        if causal:
+            hi = np.minimum(hi, i)
+        total += int(np.sum(hi - lo + 1))
+    return total
+
+
+def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False, causal: bool = False,
+                  window: int = 0):
     import torch
 
     import vision_transformer_attention_amd as vta
@@ -45,14 +62,14 @@ def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False):
     out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False)
+        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False, causal=causal, window=window)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
-        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False)
+        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False, causal=causal, window=window)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -127,6 +144,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="time only --workload (for profiling runs)")
     ap.add_argument("--out-dtype", choices=("same", "f32"), default="same",
                     help="output element type: the input's, or float32 (16-bit inputs only)")
+    ap.add_argument("--causal", action="store_true", help="aligned causal mask inside each image")
+    ap.add_argument("--window", type=int, default=0, help="key window |qi - kj| < W (0: none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -140,8 +159,12 @@ def main():
         sys.exit(1)
 
     log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
-    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup, args.out_dtype == "f32")
-    tflops = w.flops / (kernel_ms * 1e-3) / 1e12
+    masked = args.causal or args.window > 0
+    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup, args.out_dtype == "f32",
+                                               args.causal, args.window)
+    # algorithmic FLOPs: 4*D*H per (query, key) pair the mask keeps
+    flops = (4.0 * w.head_dim * w.n_heads * visible_pairs(w.lengths, args.causal, args.window)) if masked else w.flops
+    tflops = flops / (kernel_ms * 1e-3) / 1e12
     log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -153,7 +176,7 @@ def main():
         log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written once")
         del src, dst
     sec = None
-    if args.workload != SECONDARY and not args.no_secondary:
+    if args.workload != SECONDARY and not args.no_secondary and not masked:
         log(f"[bench] timing {SECONDARY}")
         w2, k2, wall2, cfg2 = time_workload(SECONDARY, max(args.steps, 200), args.warmup)
         sec = {"workload": SECONDARY, "value": w2.flops / (k2 * 1e-3) / 1e12, "unit": "TFLOP/s",
@@ -183,12 +206,14 @@ def main():
         "config": {
             "workload": w.name, "lengths": list(w.lengths), "tokens": w.total_tokens, "heads": w.n_heads,
             "head_dim": w.head_dim, "kv_heads": w.kv_heads, "out_dtype": "f32" if args.out_dtype == "f32" else w.dtype,
-            "flops_per_step": w.flops, "block_m": cfg["block_m"],
+            "causal": bool(args.causal), "window": args.window,
+            "flops_per_step": flops, "block_m": None if masked else cfg["block_m"],
             "block_n": cfg["block_n"], "waves_per_workgroup": cfg["waves"], "grid": cfg["grid"],
         },
         "roofline": {
             "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": tflops / peak, "traffic": load_traffic(w.name) if args.out_dtype == "same" else None,
+            "frac": tflops / peak,
+            "traffic": load_traffic(w.name) if args.out_dtype == "same" and not masked else None,
         },
         "secondary": sec,
         "cpu_baseline": cpu,

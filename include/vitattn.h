@@ -21,8 +21,9 @@
  * For every sequence s in [0, n_seqs), every head h and every token row
  * i in [cu_seqlens[s], cu_seqlens[s+1]):
  *     o[i,h,:] = sum_j softmax_j(scale * q[i,h,:] . k[j,g,:]) * v[j,g,:]
- * with j over the same range [cu_seqlens[s], cu_seqlens[s+1]), and g = h
- * (vitattn_fwd) or g = h / (n_heads / n_kv_heads) (vitattn_fwd_gqa).
+ * with j over the same range [cu_seqlens[s], cu_seqlens[s+1]) (and, for
+ * vitattn_fwd_masked, only the keys its mask keeps), and g = h (vitattn_fwd)
+ * or g = h / (n_heads / n_kv_heads) (vitattn_fwd_gqa, vitattn_fwd_masked).
  */
 #ifndef VITATTN_H
 #define VITATTN_H
@@ -118,6 +119,34 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
                     const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
                     int32_t n_kv_heads, int32_t head_dim, float scale, int32_t dtype,
                     hipStream_t stream);
+
+/*
+ * vitattn_fwd_masked -- the grouped-query forward pass with a mask inside each
+ * sequence.  With the query at position qi and the key at position kj of the
+ * same sequence, the key takes part only if
+ *   causal == 1 : kj <= qi -- the aligned causal rule kj <= qi + (Lk - Lq) of
+ *                 "hanzo-ml 0.11.4 src/vulkan_backend.rs", doc of
+ *                 flash_attn_gpu, with as many keys as queries (Lk = Lq);
+ *   window > 0  : |qi - kj| < window -- the key window of the encoder
+ *                 attention meta in "inferencelayer 0.2.1 src/vision_gpu.rs",
+ *                 VisionGpu::forward_one, where 0 means unrestricted (the page
+ *                 gives no further definition; this band is the reading taken
+ *                 here).  With causal == 1 it keeps the query and the
+ *                 window - 1 keys before it.
+ * Both rules hold together when both are set.  Every query keeps at least
+ * itself, so every output row is defined.  The softmax runs over the kept
+ * keys only; the others get weight exactly 0.
+ *
+ * causal  : 0 or 1 (else VITATTN_ERR_INVALID_ARG, before any HIP call).
+ * window  : >= 0 (else VITATTN_ERR_INVALID_ARG).
+ * causal == 0 && window == 0 is vitattn_fwd_gqa, bit for bit (the same
+ * kernels run).  Every other argument, the validation order, the asynchrony
+ * and the error behaviour are those of vitattn_fwd_gqa.
+ */
+int vitattn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,
+                       int32_t n_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                       int32_t window, int32_t dtype, hipStream_t stream);
 
 /* Static, never-NULL description of a status code. */
 const char* vitattn_status_string(int status);

@@ -23,14 +23,14 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(q, k, v, cu, scale, stream=None, out_dtype=None):
+def run_gpu(q, k, v, cu, scale, stream=None, out_dtype=None, causal=False, window=0):
     d = torch.device(DEV)
     qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
     if stream is None:
-        o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype)
+        o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype, causal=causal, window=window)
     else:
         with torch.cuda.stream(stream):
-            o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype)
+            o = vta.fwd(qd, kd, vd, cud, scale, out_dtype=out_dtype, causal=causal, window=window)
         stream.synchronize()
     torch.cuda.synchronize()
     return o.cpu()
@@ -66,21 +66,22 @@ def sample_rows(cu: np.ndarray, bm: int = 128, extra: int = 6, seed: int = 0) ->
     return np.array(sorted(rows), np.int64)
 
 
-def check_workload(w: inputs.Workload, full: bool, rows=None, out_dtype=None):
+def check_workload(w: inputs.Workload, full: bool, rows=None, out_dtype=None, causal=False, window=0):
     say(f"[parity] {w.name}: lengths={list(w.lengths)[:10]}{'...' if len(w.lengths) > 10 else ''} "
-        f"H={w.n_heads} Hkv={w.kv_heads} D={w.head_dim} {w.dtype} out={out_dtype} seed={w.seed} full={full}")
+        f"H={w.n_heads} Hkv={w.kv_heads} D={w.head_dim} {w.dtype} out={out_dtype} seed={w.seed} full={full} "
+        f"causal={causal} window={window}")
     q, k, v, cu, scale = inputs.make(w)
-    o = run_gpu(q, k, v, cu, scale, out_dtype=out_dtype)
+    o = run_gpu(q, k, v, cu, scale, out_dtype=out_dtype, causal=causal, window=window)
     if out_dtype is not None:
         assert o.dtype == out_dtype
     assert torch.isfinite(o.float()).all()
     if full:
-        ref = oracle.attention(q, k, v, cu, scale)
+        ref = oracle.attention(q, k, v, cu, scale, causal=causal, window=window)
         err, where = max_abs_err(o, ref)
     else:
         if rows is None:
             rows = sample_rows(cu.numpy())
-        ref = oracle.attention_rows(q, k, v, cu, scale, rows)
+        ref = oracle.attention_rows(q, k, v, cu, scale, rows, causal=causal, window=window)
         err, where = max_abs_err(o, ref, rows)
     say(f"[parity] {w.name}: max-abs err {err:.3e} at {where} (tol {TOL[w.dtype]})")
     assert err <= TOL[w.dtype], (w.name, err, where)

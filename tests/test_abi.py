@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["vitattn_fwd", "vitattn_fwd_gqa", "vitattn_status_string", "vitattn_last_error", "vitattn_kernel_config"])
+        ["vitattn_fwd", "vitattn_fwd_gqa", "vitattn_fwd_masked", "vitattn_status_string", "vitattn_last_error",
+         "vitattn_kernel_config"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -103,6 +104,31 @@ def test_gqa_validation_before_any_hip_call(lib, args, status):
     a.update(args)
     rc = lib.vitattn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["cu"], a["n_seqs"], a["n_heads"], a["n_kv_heads"],
                              a["head_dim"], ctypes.c_float(a["scale"]), a["dtype"], None)
+    assert rc == status
+    if status != OK:
+        assert len(lib.vitattn_last_error()) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(causal=2), INVALID),
+    (dict(causal=-1), INVALID),
+    (dict(window=-1), INVALID),
+    (dict(window=-(2 ** 31)), INVALID),
+    (dict(causal=1, n_kv_heads=3), INVALID),   # the grouped-query checks still apply
+    (dict(causal=1, head_dim=96), BAD_HD),
+    (dict(window=4, dtype=7), BAD_DT),
+    (dict(causal=1, scale=float("nan")), INVALID),
+    (dict(causal=1, cu=FAKE + 1), INVALID),
+    (dict(causal=1, window=5, n_seqs=0), OK),
+    (dict(causal=2, n_seqs=0), INVALID),       # a bad mask is an error even with nothing to do
+])
+def test_masked_validation_before_any_hip_call(lib, args, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, cu=FAKE, n_seqs=1, n_heads=8, n_kv_heads=2, head_dim=80, scale=0.1,
+             causal=0, window=0, dtype=1)
+    a.update(args)
+    rc = lib.vitattn_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["cu"], a["n_seqs"], a["n_heads"],
+                                a["n_kv_heads"], a["head_dim"], ctypes.c_float(a["scale"]), a["causal"],
+                                a["window"], a["dtype"], None)
     assert rc == status
     if status != OK:
         assert len(lib.vitattn_last_error()) > 0

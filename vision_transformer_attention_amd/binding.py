@@ -2,7 +2,8 @@
 
 Every step of the attention runs in the HIP library; this module checks the
 torch tensors' shapes, dtypes, devices and layout, then passes raw device
-pointers and the current HIP stream to ``vitattn_fwd``.  There is no fallback:
+pointers and the current HIP stream to ``vitattn_fwd`` (or its grouped-query and
+masked variants).  There is no fallback:
 if the library is missing or the call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -50,6 +51,8 @@ def load_library(path: str | None = None):
     lib.vitattn_fwd.restype = ctypes.c_int
     lib.vitattn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp]
     lib.vitattn_fwd_gqa.restype = ctypes.c_int
+    lib.vitattn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, i32, i32, vp]
+    lib.vitattn_fwd_masked.restype = ctypes.c_int
     lib.vitattn_status_string.argtypes = [ctypes.c_int]
     lib.vitattn_status_string.restype = ctypes.c_char_p
     lib.vitattn_last_error.argtypes = []
@@ -130,8 +133,18 @@ def fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_s
                                     ctypes.c_float(scale), dtype_code, stream))
 
 
-def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True, out_dtype=None):
-    """Bidirectional attention over packed sequences; returns ``o`` like ``q``.
+def fwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, n_seqs: int, n_heads: int,
+                   n_kv_heads: int, head_dim: int, scale: float, causal: int, window: int, dtype_code: int,
+                   stream: int) -> None:
+    """Direct call of the masked C entry point with raw pointers."""
+    lib = load_library()
+    _check(lib, lib.vitattn_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, cu_ptr, n_seqs, n_heads, n_kv_heads, head_dim,
+                                       ctypes.c_float(scale), causal, window, dtype_code, stream))
+
+
+def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True, out_dtype=None,
+        causal: bool = False, window: int = 0):
+    """Attention over packed sequences; returns ``o`` like ``q``.
 
     q: contiguous CUDA (HIP) tensor ``[T, H, D]`` of bfloat16 or float32, D in
     {64, 72, 80, 128}; k, v: the same dtype, ``[T, Hkv, D]`` with Hkv dividing H
@@ -140,7 +153,10 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
     same device (a CPU copy is checked on the host when ``check_cu``).  scale
     defaults to ``1/sqrt(D)``; any finite value (1.0 included) is passed through
     unchanged.  The output has q's dtype, or ``out_dtype`` (or ``out``'s dtype):
-    bfloat16 and float16 inputs may be written as float32.
+    bfloat16 and float16 inputs may be written as float32.  By default every
+    query sees every key of its sequence (bidirectional); ``causal`` keeps the
+    keys at or before the query and ``window`` > 0 the keys less than
+    ``window`` positions from it (both within the sequence).
     """
     import torch
     lib = load_library()
@@ -179,6 +195,11 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
         scale = 1.0 / math.sqrt(head_dim)
     if not math.isfinite(scale):
         raise ValueError("scale must be finite")
+    if causal not in (False, True, 0, 1):
+        raise ValueError("causal must be a bool")
+    if int(window) != window or window < 0:
+        raise ValueError("window must be an integer >= 0")
+    causal, window = int(bool(causal)), int(window)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != out_dtype or out.device != q.device or not out.is_contiguous():
@@ -189,7 +210,10 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         n_kv_heads = k.shape[1]
-        if n_kv_heads == n_heads:
+        if causal or window:
+            fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs,
+                           n_heads, n_kv_heads, head_dim, float(scale), causal, window, code, stream)
+        elif n_kv_heads == n_heads:
             fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs, n_heads,
                     head_dim, float(scale), code, stream)
         else:

@@ -82,6 +82,37 @@ struct PlanLds {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// P.prefix[r] = count(0) + ... + count(r - 1) for r = 0 .. n (n >= 1); returns P.prefix[n].
+// Thread tid owns positions [tid*per, tid*per + per).
+template <int NT, class F>
+__device__ int scan_to_prefix(PlanLds& P, int n, F count) {
+  const int tid = threadIdx.x;
+  const int per = ceil_div(n, NT);
+  const int beg = tid * per;
+  const int end = min(beg + per, n);
+  int local = 0;
+  for (int r = beg; r < end; ++r) local += count(r);
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) P.wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += P.wave_tot[w];
+  int run = base + incl - local;
+  if (tid == 0) P.prefix[0] = 0;
+  for (int r = beg; r < end; ++r) {
+    run += count(r);
+    P.prefix[r + 1] = run;
+  }
+  __syncthreads();
+  return P.prefix[n];
+}
+
 // Fills P for sequences [0, n) of `cu` (n >= 1).  Returns the item count.
 template <int NT>
 __device__ int build_plan(PlanLds& P, const int32_t* __restrict__ cu, int n, int n_heads, int bm) {
@@ -102,36 +133,39 @@ __device__ int build_plan(PlanLds& P, const int32_t* __restrict__ cu, int n, int
     for (int i = tid; i < n; i += NT) P.order[i] = i;
   }
   __syncthreads();
-  // Exclusive scan of items per sorted position: thread tid owns positions
-  // [tid*per, tid*per + per).
-  const int per = ceil_div(n, NT);
-  const int beg = tid * per;
-  const int end = min(beg + per, n);
-  int local = 0;
-  for (int r = beg; r < end; ++r) {
+  return scan_to_prefix<NT>(P, n, [&](int r) {
     const int s = P.order[r];
-    local += ceil_div(P.cu[s + 1] - P.cu[s], bm) * n_heads;
-  }
-  const int lane = tid & 63, wave = tid >> 6;
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) P.wave_tot[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += P.wave_tot[w];
-  int run = base + incl - local;
-  if (tid == 0) P.prefix[0] = 0;
-  for (int r = beg; r < end; ++r) {
-    const int s = P.order[r];
-    run += ceil_div(P.cu[s + 1] - P.cu[s], bm) * n_heads;
-    P.prefix[r + 1] = run;
-  }
-  __syncthreads();
-  return P.prefix[n];
+    return ceil_div(P.cu[s + 1] - P.cu[s], bm) * n_heads;
+  });
+}
+
+// Causal launches: an item's cost grows with its query block's index k inside the image
+// (it reads the keys of blocks 0 .. k), so the items are listed by decreasing cost
+// instead.  The items of block index k (one per image longer than k*bm and head) form a
+// level; levels run from the largest k down, and within a level the images go longest
+// first with the heads fastest.  Dealt out in alternating rounds, the list then pairs
+// costly items with cheap ones.  P.prefix[p] becomes the items before level p (block index
+// K-1-p), p = 0 .. K.  Needs the length-sorted order (n <= kSortMax) and K <= kMaxSeqs
+// levels, and runs after build_plan; returns K, or 0 (the sequence plan stays).
+template <int NT>
+__device__ int build_levels(PlanLds& P, int n, int n_heads, int bm) {
+  if (n > kSortMax) return 0;
+  const int maxl = P.cu[P.order[0] + 1] - P.cu[P.order[0]];
+  const int K = ceil_div(maxl, bm);
+  if (K < 1 || K > kMaxSeqs) return 0;
+  __syncthreads();  // every thread has read the sequence plan's prefix (the item count)
+  scan_to_prefix<NT>(P, K, [&](int p) {
+    // images longer than k*bm, k = K-1-p: a prefix of the longest-first order
+    const int thr = (K - 1 - p) * bm;
+    int lo = 0, hi = n;  // first sorted position whose image is not longer than thr
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int s = P.order[mid];
+      if (P.cu[s + 1] - P.cu[s] > thr) lo = mid + 1; else hi = mid;
+    }
+    return lo * n_heads;
+  });
+  return K;
 }
 
 struct Item {
@@ -154,6 +188,44 @@ __device__ __forceinline__ Item map_item(const PlanLds& P, int n, int it, int bm
   const int local = it - P.prefix[lo];
   r.head = local / tiles;
   r.q0 = r.a + (local % tiles) * bm;
+  return r;
+}
+
+// Masks ("hanzo-ml 0.11.4 src/vulkan_backend.rs", flash_attn_gpu doc: aligned causal, key
+// kj <= query qi + (Lk - Lq), which inside one image (Lk = Lq) is kj <= qi; and the encoder
+// attention's key window of "inferencelayer 0.2.1 src/vision_gpu.rs", read as
+// |qi - kj| < window with 0 = no window).  Positions are global token rows here: both rules
+// compare differences of rows of the same image, so the image's start cancels.
+__device__ __forceinline__ bool key_visible(int i, int j, int causal, int window) {
+  return (!causal | (j <= i)) & ((window <= 0) | ((j - i < window) & (i - j < window)));
+}
+
+// Narrows the keys [ka, kb) of an item (queries [q0, qend)) to those some query sees.  The
+// result is never empty: query q0 sees itself.
+// (Token rows are below 2^31 - 64, so differences of rows and keys never overflow; the
+// window is only ever compared with such differences, never added to a row.)
+__device__ __forceinline__ void mask_key_range(int& ka, int& kb, int q0, int qend, int causal, int window) {
+  if (window > 0) {
+    ka = max(ka, q0 - window + 1);              // q0 >= 0: no overflow
+    if (window <= kb - qend) kb = qend - 1 + window;  // kb = min(kb, qend - 1 + window)
+  }
+  if (causal) kb = min(kb, qend);
+}
+
+// Item `it` of a level plan of K levels (build_levels).
+__device__ __forceinline__ Item map_item_levels(const PlanLds& P, int K, int it, int bm, int n_heads) {
+  int lo = 0, hi = K;  // P.prefix[lo] <= it < P.prefix[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P.prefix[mid] <= it) lo = mid; else hi = mid;
+  }
+  const int local = it - P.prefix[lo];
+  const int s = P.order[local / n_heads];
+  Item r;
+  r.a = P.cu[s];
+  r.b = P.cu[s + 1];
+  r.head = local % n_heads;
+  r.q0 = r.a + (K - 1 - lo) * bm;
   return r;
 }
 
@@ -312,11 +384,12 @@ struct F32Traits {
 // ----------------------------------------------------------------------------
 // The attention kernel (persistent).
 // ----------------------------------------------------------------------------
-template <class T>
+template <class T, bool MASK>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const typename T::elem_t* __restrict__ q, const typename T::elem_t* __restrict__ k,
     const typename T::elem_t* __restrict__ v, typename T::elem_t* __restrict__ o,
-    const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2, int negate) {
+    const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2, int negate, int causal,
+    int window) {
   using elem_t = typename T::elem_t;
   const int kv_group = n_heads / n_kv_heads;  // query heads per K/V head
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -334,6 +407,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const Item item = map_item(plan, n_seqs, it, T::BM);
     const int qend = min(item.q0 + T::BM, item.b);
     const int row0 = item.q0 + wave * T::NQ;
+    int klo = item.a, khi = item.b;  // the keys that some row of the item sees
+    if constexpr (MASK) mask_key_range(klo, khi, item.q0, qend, causal, window);
 
     typename T::QOp Q;
     T::load_q(Q, q, row0, qend, item.head, n_heads, negate != 0, lane);
@@ -347,31 +422,47 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
     for (int qb = 0; qb < T::QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
 
-    const int ntiles = ceil_div(item.b - item.a, T::BN);
+    const int ntiles = ceil_div(khi - klo, T::BN);
     typename T::Pre pre;
     __syncthreads();  // the previous item is done with both stage buffers
     const int kv_head = item.head / kv_group;
-    T::fetch(pre, k, v, item.a, item.b, kv_head, n_kv_heads);
+    T::fetch(pre, k, v, klo, khi, kv_head, n_kv_heads);
     T::store(pre, stage);
 
     for (int t = 0; t < ntiles; ++t) {
       __syncthreads();  // tile t is in LDS; buffer (t+1)&1 is free
       const elem_t* cur = stage + (t & 1) * T::STAGE_ELEMS;
-      const int key0 = item.a + t * T::BN;
-      if (t + 1 < ntiles) T::fetch(pre, k, v, key0 + T::BN, item.b, kv_head, n_kv_heads);
+      const int key0 = klo + t * T::BN;
+      if (t + 1 < ntiles) T::fetch(pre, k, v, key0 + T::BN, khi, kv_head, n_kv_heads);
 
       f32x4_t S[T::NKB][T::QB];
       T::qk(S, Q, cur, lane);
 
-      const bool ragged = key0 + T::BN > item.b;  // last tile runs past the sequence
-      if (ragged) {  // keys past the sequence take no part in the max ...
+      // Keys past the range, and with a mask the keys a row does not see, take no part in
+      // the max and get weight exactly 0 below.
+      const bool ragged = key0 + T::BN > khi;  // last tile runs past the range
+      bool vis[T::NKB][T::QB][4];
+      bool partial = ragged;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < T::QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = key0 + kb * 16 + 4 * g + r;
+            bool ok = j < khi;
+            if constexpr (MASK) ok = ok && key_visible(min(row0 + qb * 16 + c, qend - 1), j, causal, window);
+            vis[kb][qb][r] = ok;
+          }
+      if constexpr (MASK) partial = true;
+      if (partial) {
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key0 + kb * 16 + 4 * g + r >= item.b)
+          for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
-              for (int qb = 0; qb < T::QB; ++qb) S[kb][qb][r] = -INFINITY;
+            for (int r = 0; r < 4; ++r)
+              if (!vis[kb][qb][r]) S[kb][qb][r] = -INFINITY;
       }
 
       float alpha[T::QB];
@@ -387,7 +478,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mc = mx * c2;
         alpha[qb] = 1.f;
-        if (mc > m[qb] + kLazyTau) {
+        if (mx != -INFINITY && mc > m[qb] + kLazyTau) {  // (a masked row may see no key here)
           alpha[qb] = exp2f(m[qb] - mc);
           m[qb] = mc;
           raise = true;
@@ -408,14 +499,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             S[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][r], c2, -m[qb]));
-      if (ragged) {  // ... and get weight exactly 0 (also when the scale is 0)
+      if (partial) {  // weight exactly 0 (also when the scale is 0 or the row is not set yet)
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key0 + kb * 16 + 4 * g + r >= item.b)
+          for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
-              for (int qb = 0; qb < T::QB; ++qb) S[kb][qb][r] = 0.f;
+            for (int r = 0; r < 4; ++r)
+              if (!vis[kb][qb][r]) S[kb][qb][r] = 0.f;
       }
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
@@ -712,6 +803,11 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
 //
 // Only the FIRST step of an item can hold keys outside the sequence: its first `kinv`
 // keys, which take no part in the max and get weight exactly 0 (also when c2 is 0).
+template <class C, bool PREFETCH>
+__device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
+                                              f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
+                                              const __bf16* Ks, int kb_next);
+
 template <class C, bool FIRST, bool PREFETCH = false>
 __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
@@ -774,6 +870,15 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
       }
     }
   }
+  weights_pv_32<C, PREFETCH>(S, Vs, kb0, O, lane, knext, Ks, kb_next);
+}
+
+// The weights exp2(t) of one 32-key step (t = c2*s - M per element, -inf for no weight),
+// rounded to the element kind, and O^T += V^T.P^T with the row sums alongside.
+template <class C, bool PREFETCH>
+__device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
+                                              f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
+                                              const __bf16* Ks, int kb_next) {
   // The V^T reads are issued only now, after every score MFMA of the step has been
   // consumed: an LDS read may then reuse those MFMAs' operand registers safely, and its
   // latency still hides behind the exponentials.
@@ -845,6 +950,59 @@ __device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, co
   softmax_pv_32<C, false, PREFETCH>(S, Vs, kb0, O, negM, c2, 0, lane, &knext, Ks, kb0 + C::KSUB);
 }
 
+// Q^T operands: lane (c, g) holds row row0+qb*16+c (rows past qend repeat row qend-1),
+// dims ks*32+8g..+8, and for the 16-deep tail dims NK32*32+4g..+4 (zero past D).  A
+// negative scale is folded into Q by flipping its sign bits.
+template <class C>
+__device__ __forceinline__ void load_q16(bf16x8_t (&Q)[C::QB][C::NK32], s16x4_t (&QT)[C::QB],
+                                         const __bf16* __restrict__ q, int row0, int qend, int head, int n_heads,
+                                         int negate, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int row = min(row0 + qb * 16 + c, qend - 1);
+    const __bf16* qrow = q + ((size_t)row * n_heads + head) * C::D;
+#pragma unroll
+    for (int ks = 0; ks < C::NK32; ++ks) {
+      u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
+      if (negate) w ^= 0x80008000u;
+      Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    u32x2_t t = {0u, 0u};
+    if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
+    if (negate) t ^= 0x80008000u;
+    QT[qb] = __builtin_bit_cast(s16x4_t, t);
+  }
+}
+
+// Epilogue: O / l for the rows of this wavefront that lie in the sequence, rounded to the
+// output kind.
+template <class C>
+__device__ __forceinline__ void store_o16(void* __restrict__ o, const f32x4_t (&O)[C::NACC][C::QB], int row0,
+                                          int qend, int head, int n_heads, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const float inv = 1.0f / O[C::NDB][qb][0];
+    const int row = row0 + qb * 16 + c;
+    if (row < qend) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d0 = db * 16 + 4 * g;
+        if (d0 < C::D) {
+          const f32x4_t x = O[db][qb];
+          const size_t at = ((size_t)row * n_heads + head) * C::D + d0;
+          if constexpr (C::OF32)
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + at) = x * inv;
+          else
+            *reinterpret_cast<u32x2_t*>(static_cast<__bf16*>(o) + at) =
+                u32x2_t{cvt_pk<C::E>(x[0] * inv, x[1] * inv), cvt_pk<C::E>(x[2] * inv, x[3] * inv)};
+        }
+      }
+    }
+  }
+}
+
 // One work item (sequence, head, BM queries from q0) for the whole workgroup.  The K/V
 // stage buffers and the DMA offsets depend only on head_dim and the tile shape, so work
 // items of different query-block sizes (C::QB) share them.
@@ -858,7 +1016,6 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
                                          int n_kv_heads, int kv_group, float c2, int negate, lds_u8_t* stage,
                                          unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave,
                                          int lane) {
-  const int g = lane >> 4, c = lane & 15;
   const int kv_head = item.head / kv_group;  // K/V rows are [T, n_kv_heads, D]
   const int qend = min(item.q0 + C::BM, item.b);
   const int row0 = item.q0 + wave * C::NQ;
@@ -872,25 +1029,9 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   else
     Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
 
-  // Q^T operands: lane (c, g) holds row row0+qb*16+c, dims ks*32+8g..+8, and for the
-  // 16-deep tail dims NK32*32+4g..+4 (zero past D)
   bf16x8_t Q[C::QB][C::NK32];
   s16x4_t QT[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int row = min(row0 + qb * 16 + c, qend - 1);
-    const __bf16* qrow = q + ((size_t)row * n_heads + item.head) * C::D;
-#pragma unroll
-    for (int ks = 0; ks < C::NK32; ++ks) {
-      u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
-      if (negate) w ^= 0x80008000u;
-      Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-    u32x2_t t = {0u, 0u};
-    if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
-    if (negate) t ^= 0x80008000u;
-    QT[qb] = __builtin_bit_cast(s16x4_t, t);
-  }
+  load_q16<C>(Q, QT, q, row0, qend, item.head, n_heads, negate, lane);
 
   f32x4_t O[C::NACC][C::QB];
 #pragma unroll
@@ -934,38 +1075,232 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
   }
 
-  // ---- epilogue: O / l for the rows of this wavefront that lie in the sequence
+  store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);
+}
+
+// ----------------------------------------------------------------------------
+// Masked attention (aligned causal and/or a key window; mask rules at key_visible).
+//
+// An item's keys narrow to [klo, khi), the keys some of its queries see
+// (mask_key_range), covered as in run_item by tiles that end at khi.  Each wavefront
+// classifies each 32-key step against its own query rows: no key seen by any row (the
+// step is skipped), every key seen by every row (the unmasked step, once every row has an
+// exponent offset), or partial.  A partial step masks element by element, and a row may
+// have no offset yet (negM = +inf: none of its keys so far was visible); such a row takes
+// its offset from the first step in which it sees a key, exactly as the first step of an
+// unmasked item does.
+// ----------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void step_32_masked(const __bf16* Ks, const __bf16* Vs, int kb0, int key_s,
+                                               const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                               f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2,
+                                               int lane, int row0, int qend, int a, int causal, int window,
+                                               bool use_lo, bool use_hi) {
+  const int g = lane >> 4, c = lane & 15;
+  f32x4_t S[2][C::QB];
+  {
+    KFrag<C> kf;
+    load_k<C>(kf, Ks, kb0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_32<C>(S, kf, Q, QT);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Element (kb, r) of the lane holds key j = key_s + 4g + u with u = kb*16 + r, and every
+  // rule bounds u for the row: j >= a iff u >= a - key_s - 4g; with d = i - key_s - 4g,
+  // j <= i iff u <= d, and |i - j| < window iff d - (window - 1) <= u <= d + (window - 1)
+  // (saturated: the window may exceed any row difference).  So each element costs a
+  // comparison with a constant against the row's bound, made opaque so that it is computed
+  // here once per row, not rewritten per element.  use_lo / use_hi (uniform) say whether a
+  // lower / upper bound can cut any key of the step for any row of the wavefront.
+  float tm[C::QB];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    const float inv = 1.0f / O[C::NDB][qb][0];
-    const int row = row0 + qb * 16 + c;
-    if (row < qend) {
+    const int d = min(row0 + qb * 16 + c, qend - 1) - key_s - 4 * g;  // rows past the item act as its last row
+    if (use_lo) {
+      int lo = a - key_s - 4 * g, t;
+      if (window > 0) lo = max(lo, __builtin_sub_overflow(d, window - 1, &t) ? (int)0x80000000 : t);
+      asm volatile("" : "+v"(lo));
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const int d0 = db * 16 + 4 * g;
-        if (d0 < C::D) {
-          const f32x4_t x = O[db][qb];
-          const size_t at = ((size_t)row * n_heads + item.head) * C::D + d0;
-          if constexpr (C::OF32)
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + at) = x * inv;
-          else
-            *reinterpret_cast<u32x2_t*>(static_cast<__bf16*>(o) + at) =
-                u32x2_t{cvt_pk<C::E>(x[0] * inv, x[1] * inv), cvt_pk<C::E>(x[2] * inv, x[3] * inv)};
-        }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb * 16 + r < lo) S[kb][qb][r] = -INFINITY;
+    }
+    if (use_hi) {
+      int hi = causal ? d : 0x7fffffff, t;
+      if (window > 0) hi = min(hi, __builtin_add_overflow(d, window - 1, &t) ? 0x7fffffff : t);
+      asm volatile("" : "+v"(hi));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb * 16 + r > hi) S[kb][qb][r] = -INFINITY;
+    }
+    float x = S[0][qb][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = fmaxf(x, S[kb][qb][r]);
+    tm[qb] = max_4groups(x);  // the same in the four lanes of the row
+  }
+  // A row that sees a key here and whose max leaves the exponent window (always the case
+  // for a row without an offset, negM = +inf) moves its offset to this max and rescales its
+  // running output and row sum (by 0 for a row without an offset, whose are 0).  Rare after
+  // the first visible step, so one vote skips it for the whole wavefront.
+  bool need[C::QB], any = false;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    need[qb] = tm[qb] != -INFINITY && __builtin_fmaf(tm[qb], c2, negM[qb]) >= kRaise<C::E>;
+    any = any || need[qb];
+  }
+  if (__any(any)) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      if (need[qb]) {
+        const float nm = -__builtin_fmaf(tm[qb], c2, kHead<C::E>);
+        const float alpha = __builtin_amdgcn_exp2f(nm - negM[qb]);
+#pragma unroll
+        for (int db = 0; db < C::NACC; ++db) O[db][qb] *= alpha;
+        negM[qb] = nm;
       }
     }
   }
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = S[kb][qb][r];
+        S[kb][qb][r] = x == -INFINITY ? -INFINITY : __builtin_fmaf(x, c2, negM[qb]);
+      }
+  weights_pv_32<C, false>(S, Vs, kb0, O, lane, nullptr, nullptr, 0);
 }
 
-// The bf16 kernel.  CA and CB differ only in the queries per wavefront (CA::QB > CB::QB).
+template <class C>
+__device__ __forceinline__ void run_item_masked(const Item& item, const __bf16* __restrict__ q,
+                                                const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                                void* __restrict__ o, int n_heads, int n_kv_heads, int kv_group,
+                                                float c2, int negate, int causal, int window, lds_u8_t* stage,
+                                                unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE],
+                                                int wave, int lane) {
+  const int kv_head = item.head / kv_group;
+  const int qend = min(item.q0 + C::BM, item.b);
+  const int row0 = item.q0 + wave * C::NQ;
+  int klo = item.a, khi = item.b;
+  mask_key_range(klo, khi, item.q0, qend, causal, window);
+  const int ntiles = ceil_div(khi - klo, C::BN);
+  const int pad = ntiles * C::BN - (khi - klo);  // 0 <= pad < BN
+  const int kstart = klo - pad;                   // key of tile 0's row 0
+  // this wavefront's query rows, clamped into the item like the Q rows
+  const int wlo = min(row0, qend - 1), whi = min(row0 + C::NQ - 1, qend - 1);
+  const bool idle = row0 >= qend;  // no row of the wavefront lies in the sequence
+
+  __syncthreads();  // the previous item is done with both stage buffers
+  if (pad > 0)
+    Dma<C>::template issue<true>(k, v, stage, klo, khi, pad, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+  else
+    Dma<C>::template issue<false>(k, v, stage, klo, khi, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+
+  bf16x8_t Q[C::QB][C::NK32];
+  s16x4_t QT[C::QB];
+  load_q16<C>(Q, QT, q, row0, qend, item.head, n_heads, negate, lane);
+
+  f32x4_t O[C::NACC][C::QB];
+  float negM[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    negM[qb] = INFINITY;  // no offset yet
+#pragma unroll
+    for (int db = 0; db < C::NACC; ++db) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  bool ready = false;  // every row of the wavefront has an offset
+
+  // The tiles whose 64 keys every row of this wavefront sees form one run [f0, f1): the
+  // keys visible to all of the rows [wlo, whi] are [ka, kz] below.  Before and after the
+  // run, each 32-key step is skipped when no row sees a key of it and otherwise masked
+  // element by element; the run itself takes the unmasked tile body (after one masked
+  // tile if some row still has no offset).  The three phases are separate loops, each
+  // with one barrier per tile like every other wavefront's, so that the register
+  // allocation of the unmasked body is not shared with the masked steps.
+  int ka = item.a, kz = item.b - 1;
+  if (causal) kz = min(kz, wlo);
+  if (window > 0) {
+    ka = max(ka, whi - window + 1);
+    if (window - 1 <= kz - wlo) kz = wlo + window - 1;  // kz = min(kz, wlo + window - 1)
+  }
+  int f0 = ceil_div(ka - kstart, C::BN);       // ka >= klo >= kstart
+  int f1 = min(ntiles, (kz - kstart + 1) / C::BN);  // kz >= wlo >= kstart
+  if (idle || f1 <= f0) f0 = f1 = ntiles;      // no run: every tile is masked (or skipped)
+
+  // one tile: wait for its DMA, let every wave pass the barrier, start the next tile's DMA
+  auto begin_tile = [&](int t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+    __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+    if (t + 1 < ntiles)
+      Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, khi, 0,
+                                    kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+  };
+  // the masked steps of tile t
+  auto masked_tile = [&](int t) {
+    if (idle) return;
+    const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
+    const __bf16* Ks = (const __bf16*)(buf);
+    const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const int s = kstart + t * C::BN + sub * C::KSUB, e = s + C::KSUB - 1;  // the step's keys [s, e]
+      const bool none = e < item.a || (causal && s > whi) || (window > 0 && (wlo - e >= window || s - whi >= window));
+      if (none) continue;
+      step_32_masked<C>(Ks, Vs, sub * C::KSUB, s, Q, QT, O, negM, c2, lane, row0, qend, item.a, causal, window,
+                        s < ka, e > kz);
+    }
+    bool set = true;
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) set = set && negM[qb] != INFINITY;
+    ready = __all(set);
+  };
+
+  int t = 0;
+  for (; t < f0; ++t) {
+    begin_tile(t);
+    masked_tile(t);
+  }
+  if (t < f1 && !ready) {  // the run's first tile sets the offsets of the rows still without one
+    begin_tile(t);
+    masked_tile(t);
+    ++t;
+  }
+  for (; t < f1; ++t) {  // every row has an offset and sees every key of the tile
+    begin_tile(t);
+    const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
+    const __bf16* Ks = (const __bf16*)(buf);
+    const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
+    KFrag<C> k0, k1;
+    load_k<C>(k0, Ks, 0, lane);
+    step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+    step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+  }
+  for (; t < ntiles; ++t) {
+    begin_tile(t);
+    masked_tile(t);
+  }
+  store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);
+}
+
+// The bf16 kernel.  CA and CB differ only in the queries per wavefront (CA::QB >= CB::QB).
 // The launch works with CA's large query blocks unless they would leave most of the grid
 // idle (a short single image), in which case it re-plans with CB's small blocks: more
 // items, so more of the machine works, each item over the same keys.
-template <class CA, class CB>
+template <class CA, class CB, bool MASK>
 __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     void* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs, int n_heads, int n_kv_heads, float c2,
-    int negate) {
+    int negate, int causal, int window) {
   static_assert(CA::D == CB::D && CA::NW == CB::NW && CA::BN == CB::BN && CA::STAGE_BYTES == CB::STAGE_BYTES &&
                     CA::E == CB::E && CA::OF32 == CB::OF32,
                 "the two query-block sizes share the staging layout and the element kinds");
@@ -981,6 +1316,10 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CB::BM);
   }
   const int bm = small ? CB::BM : CA::BM;
+  int levels = 0;  // a causal launch lists its items by decreasing cost when it can
+  if constexpr (MASK) {
+    if (causal) levels = build_levels<CA::NT>(plan, n_seqs, n_heads, bm);
+  }
   // the wave index and every item field are uniform across a wavefront: keep them in scalar
   // registers, so that the per-tile DMA issue is scalar address arithmetic
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1002,15 +1341,26 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (xj >= cnt) break;  // only the last round can leave a workgroup without an item
     const int kk = lo + xj;
     const int it = base + ((round & 1) ? m - 1 - kk : kk);
-    Item item = map_item(plan, n_seqs, it, bm);
+    Item item = levels ? map_item_levels(plan, levels, it, bm, n_heads) : map_item(plan, n_seqs, it, bm);
     item.a = __builtin_amdgcn_readfirstlane(item.a);
     item.b = __builtin_amdgcn_readfirstlane(item.b);
     item.head = __builtin_amdgcn_readfirstlane(item.head);
     item.q0 = __builtin_amdgcn_readfirstlane(item.q0);
-    if (small)
-      run_item<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave, lane);
-    else
-      run_item<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave, lane);
+    if constexpr (MASK) {
+      if (small)
+        run_item_masked<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, causal, window, stage,
+                            row_bytes, dma_off, wave, lane);
+      else
+        run_item_masked<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, causal, window, stage,
+                            row_bytes, dma_off, wave, lane);
+    } else {
+      if (small)
+        run_item<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave,
+                     lane);
+      else
+        run_item<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave,
+                     lane);
+    }
   }
 }
 
@@ -1033,10 +1383,10 @@ struct KernelDesc {
   size_t lds;
 };
 
-template <class T>
+template <class T, bool MASK>
 KernelDesc describe_f32() {
   KernelDesc d;
-  d.func = reinterpret_cast<const void*>(&attn_fwd_f32_kernel<T>);
+  d.func = reinterpret_cast<const void*>(&attn_fwd_f32_kernel<T, MASK>);
   d.bm = T::BM;
   d.bn = T::BN;
   d.waves = T::NW;
@@ -1045,10 +1395,10 @@ KernelDesc describe_f32() {
   return d;
 }
 
-template <class C, class CB>
+template <class C, class CB, bool MASK>
 KernelDesc describe_bf16() {
   KernelDesc d;
-  d.func = reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C, CB>);
+  d.func = reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<C, CB, MASK>);
   d.bm = C::BM;
   d.bn = C::BN;
   d.waves = C::NW;
@@ -1075,13 +1425,29 @@ template <int D, int E, bool OF32>
 using KCfg = Bf16Cfg<D, D == 128 ? VITATTN_BF16_QB_128 : VITATTN_BF16_QB, VITATTN_BF16_NW, 64, E, OF32>;
 template <int D, int E, bool OF32>
 using SCfg = Bf16Cfg<D, VITATTN_BF16_QB_SMALL, VITATTN_BF16_NW, 64, E, OF32>;
+// masked kernels: the large query blocks of the unmasked kernel for a causal mask or a wide
+// window, and 2 blocks per wavefront (1 at head_dim 128) for a narrow window, whose items
+// see fewer keys beyond their own rows when they are shorter
+#ifndef VITATTN_BF16_QB_NARROW
+#define VITATTN_BF16_QB_NARROW 2
+#endif
+#ifndef VITATTN_BF16_QB_NARROW_128
+#define VITATTN_BF16_QB_NARROW_128 1
+#endif
+template <int D, int E, bool OF32>
+using NCfg = Bf16Cfg<D, D == 128 ? VITATTN_BF16_QB_NARROW_128 : VITATTN_BF16_QB_NARROW, VITATTN_BF16_NW, 64, E, OF32>;
+// a window is narrow when a query sees fewer keys than this (2*window - 1, or window with
+// the causal rule): there the shorter items waste less than the larger ones gain
+constexpr long long kNarrowKeys = 1024;
 using K_f32_64 = F32Traits<64, 1, 4, 32>;
 using K_f32_72 = F32Traits<72, 1, 4, 32>;
 using K_f32_80 = F32Traits<80, 1, 4, 32>;
 using K_f32_128 = F32Traits<128, 1, 4, 32>;
 
-// Kernel table index: dtype * 4 + head_dim slot (dtype codes as in vitattn_dtype_t).
-int kernel_index(int32_t head_dim, int32_t dtype) {
+// Kernel table index: (mask kind * 5 + dtype) * 4 + head_dim slot, with dtype codes as in
+// vitattn_dtype_t and mask kind 0 (none), 1 (causal or a wide window: the masked kernel with
+// the large query blocks) or 2 (a narrow window: the masked kernel with small ones).
+int kernel_index(int32_t head_dim, int32_t dtype, int mask_kind = 0) {
   int hd;
   switch (head_dim) {
     case 64: hd = 0; break;
@@ -1090,37 +1456,59 @@ int kernel_index(int32_t head_dim, int32_t dtype) {
     case 128: hd = 3; break;
     default: return -1;
   }
-  return dtype * 4 + hd;
+  return (mask_kind * 5 + dtype) * 4 + hd;
 }
 
-template <int E, bool OF32>
+int mask_kind_of(int32_t causal, int32_t window) {
+  if (!causal && window <= 0) return 0;
+  if (window <= 0) return 1;
+  const long long seen = causal ? (long long)window : 2LL * window - 1;
+  return seen < kNarrowKeys ? 2 : 1;
+}
+
+template <int E, bool OF32, int MK>
 KernelDesc describe16(int hd) {
-  switch (hd) {
-    case 0: return describe_bf16<KCfg<64, E, OF32>, SCfg<64, E, OF32>>();
-    case 1: return describe_bf16<KCfg<72, E, OF32>, SCfg<72, E, OF32>>();
-    case 2: return describe_bf16<KCfg<80, E, OF32>, SCfg<80, E, OF32>>();
-    default: return describe_bf16<KCfg<128, E, OF32>, SCfg<128, E, OF32>>();
+  if constexpr (MK == 2) {
+    switch (hd) {
+      case 0: return describe_bf16<NCfg<64, E, OF32>, SCfg<64, E, OF32>, true>();
+      case 1: return describe_bf16<NCfg<72, E, OF32>, SCfg<72, E, OF32>, true>();
+      case 2: return describe_bf16<NCfg<80, E, OF32>, SCfg<80, E, OF32>, true>();
+      default: return describe_bf16<NCfg<128, E, OF32>, SCfg<128, E, OF32>, true>();
+    }
+  } else {
+    switch (hd) {
+      case 0: return describe_bf16<KCfg<64, E, OF32>, SCfg<64, E, OF32>, MK == 1>();
+      case 1: return describe_bf16<KCfg<72, E, OF32>, SCfg<72, E, OF32>, MK == 1>();
+      case 2: return describe_bf16<KCfg<80, E, OF32>, SCfg<80, E, OF32>, MK == 1>();
+      default: return describe_bf16<KCfg<128, E, OF32>, SCfg<128, E, OF32>, MK == 1>();
+    }
+  }
+}
+
+template <int MK>
+KernelDesc kernel_desc_of(int dtype, int hd) {
+  switch (dtype) {
+    case VITATTN_DTYPE_F32:  // one masked float32 kernel serves both mask kinds
+      switch (hd) {
+        case 0: return describe_f32<K_f32_64, MK != 0>();
+        case 1: return describe_f32<K_f32_72, MK != 0>();
+        case 2: return describe_f32<K_f32_80, MK != 0>();
+        default: return describe_f32<K_f32_128, MK != 0>();
+      }
+    case VITATTN_DTYPE_BF16: return describe16<kBF16, false, MK>(hd);
+    case VITATTN_DTYPE_F16: return describe16<kF16, false, MK>(hd);
+    case VITATTN_DTYPE_BF16_OUT_F32: return describe16<kBF16, true, MK>(hd);
+    default: return describe16<kF16, true, MK>(hd);
   }
 }
 
 KernelDesc kernel_desc(int idx) {
-  const int hd = idx % 4;
-  switch (idx / 4) {
-    case VITATTN_DTYPE_F32:
-      switch (hd) {
-        case 0: return describe_f32<K_f32_64>();
-        case 1: return describe_f32<K_f32_72>();
-        case 2: return describe_f32<K_f32_80>();
-        default: return describe_f32<K_f32_128>();
-      }
-    case VITATTN_DTYPE_BF16: return describe16<kBF16, false>(hd);
-    case VITATTN_DTYPE_F16: return describe16<kF16, false>(hd);
-    case VITATTN_DTYPE_BF16_OUT_F32: return describe16<kBF16, true>(hd);
-    default: return describe16<kF16, true>(hd);
-  }
+  const int hd = idx % 4, dtype = (idx / 4) % 5, mk = idx / 20;
+  if (mk == 2) return kernel_desc_of<2>(dtype, hd);
+  return mk == 1 ? kernel_desc_of<1>(dtype, hd) : kernel_desc_of<0>(dtype, hd);
 }
 
-constexpr int kNumKernels = 20;  // 5 dtype codes x 4 head dims
+constexpr int kNumKernels = 60;  // 3 mask kinds x 5 dtype codes x 4 head dims
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
@@ -1223,9 +1611,9 @@ int vitattn_kernel_config(int32_t head_dim, int32_t dtype, int32_t* block_m, int
   return VITATTN_OK;
 }
 
-int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
-                    int32_t n_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                    int32_t dtype, hipStream_t stream) {
+int vitattn_fwd_masked(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                       int32_t n_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                       int32_t causal, int32_t window, int32_t dtype, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (n_seqs < 0) return fail(VITATTN_ERR_INVALID_ARG, "n_seqs must be >= 0 (got %d)", n_seqs);
   if (n_heads <= 0) return fail(VITATTN_ERR_INVALID_ARG, "n_heads must be > 0 (got %d)", n_heads);
@@ -1235,6 +1623,8 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
   int rc = validate(head_dim, dtype);
   if (rc != VITATTN_OK) return rc;
   if (!std::isfinite(scale)) return fail(VITATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (causal != 0 && causal != 1) return fail(VITATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (window < 0) return fail(VITATTN_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
   if (n_seqs == 0) return VITATTN_OK;
   if (!q || !k || !v || !o || !cu_seqlens) return fail(VITATTN_ERR_INVALID_ARG, "null pointer argument");
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
@@ -1245,7 +1635,7 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
   DeviceState* st = nullptr;
   rc = get_device_state(&st);
   if (rc != VITATTN_OK) return rc;
-  const int idx = kernel_index(head_dim, dtype);
+  const int idx = kernel_index(head_dim, dtype, mask_kind_of(causal, window));
   const KernelDesc d = kernel_desc(idx);
   const float c2 = std::fabs(scale) * kLog2e;
   const int negate = scale < 0.0f ? 1 : 0;
@@ -1260,7 +1650,7 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
       void* oo = o;
       const int32_t* cc = cu_seqlens + s0;
       void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&n_kv_heads,
-                      (void*)&c2, (void*)&negate};
+                      (void*)&c2, (void*)&negate, (void*)&causal, (void*)&window};
       hipError_t e = hipLaunchKernel(d.func, dim3(st->grid[idx]), dim3(d.nt), args, d.lds, stream);
       if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     } else {
@@ -1270,7 +1660,7 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
       float* oo = static_cast<float*>(o);
       const int32_t* cc = cu_seqlens + s0;
       void* args[] = {&qq, &kk, &vv, &oo, (void*)&cc, (void*)&n, (void*)&n_heads, (void*)&n_kv_heads,
-                      (void*)&c2, (void*)&negate};
+                      (void*)&c2, (void*)&negate, (void*)&causal, (void*)&window};
       hipError_t e = hipLaunchKernel(d.func, dim3(st->grid[idx]), dim3(d.nt), args, d.lds, stream);
       if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     }
@@ -1278,6 +1668,13 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "after launch: %s", hipGetErrorString(e));
   return VITATTN_OK;
+}
+
+int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                    int32_t n_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                    int32_t dtype, hipStream_t stream) {
+  return vitattn_fwd_masked(q, k, v, o, cu_seqlens, n_seqs, n_heads, n_kv_heads, head_dim, scale, 0, 0, dtype,
+                            stream);
 }
 
 int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t n_seqs,

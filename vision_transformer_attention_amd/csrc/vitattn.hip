@@ -113,9 +113,10 @@ __device__ int scan_to_prefix(PlanLds& P, int n, F count) {
   return P.prefix[n];
 }
 
-// Fills P for sequences [0, n) of `cu` (n >= 1).  Returns the item count.
+// Loads the sequence bounds of `cu` (n >= 1 sequences) into P and orders the sequences
+// longest first (when n <= kSortMax; else in index order).
 template <int NT>
-__device__ int build_plan(PlanLds& P, const int32_t* __restrict__ cu, int n, int n_heads, int bm) {
+__device__ void plan_load(PlanLds& P, const int32_t* __restrict__ cu, int n) {
   const int tid = threadIdx.x;
   for (int i = tid; i <= n; i += NT) P.cu[i] = cu[i];
   __syncthreads();
@@ -133,6 +134,12 @@ __device__ int build_plan(PlanLds& P, const int32_t* __restrict__ cu, int n, int
     for (int i = tid; i < n; i += NT) P.order[i] = i;
   }
   __syncthreads();
+}
+
+// Fills P.prefix with the items (sequence, head, bm-query block) of the sequences in P's
+// order, after plan_load.  Returns the item count.
+template <int NT>
+__device__ int plan_items(PlanLds& P, int n, int n_heads, int bm) {
   return scan_to_prefix<NT>(P, n, [&](int r) {
     const int s = P.order[r];
     return ceil_div(P.cu[s + 1] - P.cu[s], bm) * n_heads;
@@ -146,7 +153,7 @@ __device__ int build_plan(PlanLds& P, const int32_t* __restrict__ cu, int n, int
 // first with the heads fastest.  Dealt out in alternating rounds, the list then pairs
 // costly items with cheap ones.  P.prefix[p] becomes the items before level p (block index
 // K-1-p), p = 0 .. K.  Needs the length-sorted order (n <= kSortMax) and K <= kMaxSeqs
-// levels, and runs after build_plan; returns K, or 0 (the sequence plan stays).
+// levels, and runs after plan_items; returns K, or 0 (the sequence plan stays).
 template <int NT>
 __device__ int build_levels(PlanLds& P, int n, int n_heads, int bm) {
   if (n > kSortMax) return 0;
@@ -396,7 +403,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   PlanLds& plan = *reinterpret_cast<PlanLds*>(smem);
   elem_t* stage = reinterpret_cast<elem_t*>(smem + ((sizeof(PlanLds) + 15) / 16) * 16);
 
-  const int n_items = build_plan<T::NT>(plan, cu, n_seqs, n_heads, T::BM);
+  plan_load<T::NT>(plan, cu, n_seqs);
+  const int n_items = plan_items<T::NT>(plan, n_seqs, n_heads, T::BM);
   T::zero_pad(stage);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -622,12 +630,17 @@ struct Dma {
     return (unsigned)row * row_bytes + (unsigned)ch * 16u;
   }
 
-  // byte offsets (relative to the tile's first key row) for full tiles
+  // byte offsets (relative to the tile's first key row) for full tiles.  Computed at the start
+  // of every work item from an opaque copy of the lane index, so that the compiler cannot hoist
+  // them out of the item loop: held for the whole launch they would be live across every
+  // kind of item and push the kernel into spilling.
   static __device__ __forceinline__ void init(unsigned (&off)[PER_WAVE], int wave, int lane, unsigned row_bytes) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int wl = wave + i * C::NW;
-      off[i] = wl < C::LOADS ? lane_offset(wl, lane, 0, row_bytes) : 0u;
+      off[i] = wl < C::LOADS ? lane_offset(wl, ln, 0, row_bytes) : 0u;
     }
   }
 
@@ -813,7 +826,10 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
                                               f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
                                               int lane, KFrag<C>* knext = nullptr, const __bf16* Ks = nullptr,
                                               int kb_next = 0) {
-  const int g = lane >> 4;
+  int g = lane >> 4;
+  // (opaque in the first step: otherwise the key positions 16kb + 4g + r it compares are
+  // hoisted out of the item loop as eight registers held for the whole launch)
+  if constexpr (FIRST) asm volatile("" : "+v"(g));
   if constexpr (FIRST) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -1014,8 +1030,9 @@ template <class C>
 __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ v, void* __restrict__ o, int n_heads,
                                          int n_kv_heads, int kv_group, float c2, int negate, lds_u8_t* stage,
-                                         unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE], int wave,
-                                         int lane) {
+                                         unsigned row_bytes, int wave, int lane) {
+  unsigned dma_off[Dma<C>::PER_WAVE];  // computed per item (see Dma::init), not held across items
+  Dma<C>::init(dma_off, wave, lane, row_bytes);
   const int kv_head = item.head / kv_group;  // K/V rows are [T, n_kv_heads, D]
   const int qend = min(item.q0 + C::BM, item.b);
   const int row0 = item.q0 + wave * C::NQ;
@@ -1076,6 +1093,113 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   }
 
   store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);
+}
+
+typedef __attribute__((address_space(3))) float lds_f32_t;
+
+// A work item of the short-image plan with the keys split inside the workgroup: the item is
+// C::NW/2 query blocks of C::NQ rows, and wavefronts 2p and 2p+1 both hold block p, each
+// taking one of the two 32-key steps of every 64-key tile (wavefront 2p+1 the second).  The
+// K/V tiles are staged once for all four wavefronts, double-buffered, as in run_item.  Each
+// wavefront keeps its own exponent offset, output and row sum over its half of the keys; at
+// the end the odd wavefront of a pair leaves them in LDS and the even one merges them in a
+// fixed order, scaling each half by 2^(its offset - the larger offset) ("inferencelayer 0.2.1
+// src/vision_gpu.rs", vis_attn_coop_src doc, "The obstacle, and the way round it": the same
+// rescale as the online update), and stores the rows.  Half the serial steps per item and
+// twice the items of run_item<C>: for a short image whose items would otherwise fill at most
+// half of the grid, where each item's chain of dependent steps sets the time.
+template <class C>
+__device__ __forceinline__ void run_item_split(const Item& item, const __bf16* __restrict__ q,
+                                               const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                               void* __restrict__ o, int n_heads, int n_kv_heads, int kv_group,
+                                               float c2, int negate, lds_u8_t* stage, unsigned row_bytes,
+                                               int wave, int lane_in) {
+  // an opaque lane index: the per-lane LDS addresses of this kind of item are computed in it,
+  // not hoisted out of the item loop beside those of the large items
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  unsigned dma_off[Dma<C>::PER_WAVE];  // computed per item (see Dma::init), not held across items
+  Dma<C>::init(dma_off, wave, lane, row_bytes);
+  static_assert(C::NSUB == 2 && C::NW % 2 == 0, "two 32-key steps per tile, wavefronts in pairs");
+  constexpr int BM = C::NW / 2 * C::NQ;  // queries per item
+  constexpr int NV = C::NACC * 4 + 1;    // floats per lane handed over: output, row sum, offset
+  static_assert(C::NW / 2 * NV * 64 * 4 <= 2 * C::STAGE_BYTES, "merge area fits the stage buffers");
+  const int kv_head = item.head / kv_group;
+  const int qend = min(item.q0 + BM, item.b);
+  const int half = wave & 1;                        // which 32 keys of each tile
+  const int row0 = item.q0 + (wave >> 1) * C::NQ;   // this pair's query block
+  const int ntiles = ceil_div(item.b - item.a, C::BN);
+  const int pad = ntiles * C::BN - (item.b - item.a);  // 0 <= pad < BN
+  const int kstart = item.a - pad;
+  auto issue_tile = [&](int t) {  // tile t >= 1 into buffer t & 1
+    Dma<C>::template issue<false>(k, v, stage + (t & 1) * C::STAGE_BYTES, kstart + t * C::BN, item.b, 0, kv_head,
+                                  n_kv_heads, row_bytes, dma_off, wave, lane);
+  };
+
+  __syncthreads();  // the previous item is done with the stage buffers (and the merge area)
+  if (pad > 0)
+    Dma<C>::template issue<true>(k, v, stage, item.a, item.b, pad, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+  else
+    Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+
+  bf16x8_t Q[C::QB][C::NK32];
+  s16x4_t QT[C::QB];
+  load_q16<C>(Q, QT, q, row0, qend, item.head, n_heads, negate, lane);
+
+  f32x4_t O[C::NACC][C::QB];
+  float negM[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    negM[qb] = INFINITY;  // no key seen yet (the merge weighs such a half by 0)
+#pragma unroll
+    for (int db = 0; db < C::NACC; ++db) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int kb0 = half * C::KSUB;  // this wavefront's step inside every tile
+  const int kinv = pad - kb0;      // leading keys of that step in tile 0 that precede the image
+  bool started = false;            // uniform: the wavefront's first step with a key has run
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile 0 has landed
+  __syncthreads();                                   // every wave's has
+  if (ntiles > 1) issue_tile(1);
+  if (kinv < C::KSUB) {  // tile 0's step holds at least one key of the image
+    step_32<C, true>((const __bf16*)stage, (const __bf16*)(stage + C::K_BYTES), kb0, max(kinv, 0), Q, QT, O, negM,
+                     c2, lane);
+    started = true;
+  }
+  for (int t = 1; t < ntiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
+    __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
+    if (t + 1 < ntiles) issue_tile(t + 1);
+    const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
+    if (started) {
+      step_32<C, false>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
+    } else {
+      step_32<C, true>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
+      started = true;
+    }
+  }
+
+  // merge the pair's halves: lane-major so that the LDS accesses are conflict free
+  __syncthreads();  // every wavefront is done reading the last tile
+  lds_f32_t* area = (lds_f32_t*)stage + (wave >> 1) * (NV * 64) + lane;
+  if (half) {
+#pragma unroll
+    for (int db = 0; db < C::NACC; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) area[(db * 4 + r) * 64] = O[db][0][r];
+    area[(NV - 1) * 64] = negM[0];
+  }
+  __syncthreads();
+  if (!half) {
+    const float other = area[(NV - 1) * 64];
+    const float nm = fminf(negM[0], other);  // the larger of the two offsets, negated
+    const float f0 = __builtin_amdgcn_exp2f(nm - negM[0]), f1 = __builtin_amdgcn_exp2f(nm - other);
+#pragma unroll
+    for (int db = 0; db < C::NACC; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[db][0][r] = O[db][0][r] * f0 + area[(db * 4 + r) * 64] * f1;
+    store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1186,8 +1310,9 @@ __device__ __forceinline__ void run_item_masked(const Item& item, const __bf16* 
                                                 const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                                                 void* __restrict__ o, int n_heads, int n_kv_heads, int kv_group,
                                                 float c2, int negate, int causal, int window, lds_u8_t* stage,
-                                                unsigned row_bytes, const unsigned (&dma_off)[Dma<C>::PER_WAVE],
-                                                int wave, int lane) {
+                                                unsigned row_bytes, int wave, int lane) {
+  unsigned dma_off[Dma<C>::PER_WAVE];  // computed per item (see Dma::init), not held across items
+  Dma<C>::init(dma_off, wave, lane, row_bytes);
   const int kv_head = item.head / kv_group;
   const int qend = min(item.q0 + C::BM, item.b);
   const int row0 = item.q0 + wave * C::NQ;
@@ -1309,13 +1434,26 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   lds_u8_t* stage = (lds_u8_t*)smem + ((sizeof(PlanLds) + 15) / 16) * 16;
 
   const int G = gridDim.x;
-  int n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CA::BM);
-  const bool small = 2 * n_items < G;  // the same decision in every workgroup
+  plan_load<CA::NT>(plan, cu, n_seqs);
+  int n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CA::BM);
+  // Every decision below depends only on cu_seqlens, so every workgroup takes the same.
+  // Short images, whose large items would fill less than half of the grid, take CB's small
+  // query blocks; unmasked, when even twice as many of those items fit in one round of the
+  // grid, each is split further between wavefront pairs by keys (run_item_split).
+  const bool small = 2 * n_items < G;
+  bool split = false;
   if (small) {
-    __syncthreads();  // everyone has read the first plan's item count
-    n_items = build_plan<CA::NT>(plan, cu, n_seqs, n_heads, CB::BM);
+    __syncthreads();  // everyone has read the item count
+    n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM);
+    if constexpr (!MASK) {
+      split = 2 * n_items <= G;
+      if (split) {
+        __syncthreads();
+        n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM / 2);
+      }
+    }
   }
-  const int bm = small ? CB::BM : CA::BM;
+  const int bm = split ? CB::BM / 2 : (small ? CB::BM : CA::BM);
   int levels = 0;  // a causal launch lists its items by decreasing cost when it can
   if constexpr (MASK) {
     if (causal) levels = build_levels<CA::NT>(plan, n_seqs, n_heads, bm);
@@ -1326,8 +1464,6 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;  // workgroups go to the 8 XCDs round-robin
   const unsigned row_bytes = (unsigned)n_kv_heads * CA::D * 2u;  // one K/V row
   const int kv_group = n_heads / n_kv_heads;                       // query heads per K/V head
-  unsigned dma_off[Dma<CA>::PER_WAVE];
-  Dma<CA>::init(dma_off, wave, lane, row_bytes);
 
   // Items in longest-first order are dealt out in rounds of G, alternating direction to
   // even out the load.  Within a round of m items, XCD x takes the contiguous run
@@ -1349,17 +1485,18 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if constexpr (MASK) {
       if (small)
         run_item_masked<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, causal, window, stage,
-                            row_bytes, dma_off, wave, lane);
+                            row_bytes, wave, lane);
       else
         run_item_masked<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, causal, window, stage,
-                            row_bytes, dma_off, wave, lane);
+                            row_bytes, wave, lane);
     } else {
-      if (small)
-        run_item<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave,
-                     lane);
+      if (split)
+        run_item_split<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, wave,
+                           lane);
+      else if (small)
+        run_item<CB>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, wave, lane);
       else
-        run_item<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, dma_off, wave,
-                     lane);
+        run_item<CA>(item, q, k, v, o, n_heads, n_kv_heads, kv_group, c2, negate, stage, row_bytes, wave, lane);
     }
   }
 }

@@ -27,6 +27,11 @@ the same sequence only.  Sources, by page title:
   ("inferencelayer 0.2.1 src/vision_gpu.rs", ``VisionGpu::forward_one``: window 0
   is unrestricted) is read as ``|qi - kj| < window``.
 
+``qkv_prologue`` is the input side of the path: the packed projection output split into Q, K and
+V, with the optional per-head RMS norm and the rope of "inferencelayer 0.2.1 src/vision_gpu.rs"
+(``VIS_QKV_ROPE``, ``GLM_QKV_QKNORM_ROPE``) and the norm definition of "hf2q
+src/inference/vision/vit_gpu.rs" (``vit_rms_norm_gpu``: eps inside the square root).
+
 Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
 hand-derived golden values, invariants, and a library routine (PyTorch's CPU
 ``scaled_dot_product_attention`` in float64).
@@ -80,6 +85,9 @@ def _bind(lib):
                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_int32,
                                                 ctypes.c_int32, i64p, ctypes.c_int64]
     lib.vitattn_ref_rows_masked_f64.restype = ctypes.c_int
+    lib.vitattn_ref_qkv_prologue_f64.argtypes = [f32p, f32p, f32p, f32p, f32p, ctypes.c_double, f64p, f64p, f64p,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.vitattn_ref_qkv_prologue_f64.restype = ctypes.c_int
     lib.vitattn_ref_row_probs_f64.argtypes = [f32p, f32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_double, ctypes.c_int64, ctypes.c_int32, f64p]
     lib.vitattn_ref_row_probs_f64.restype = ctypes.c_int64
@@ -201,6 +209,54 @@ def row_probs(q, k, cu_seqlens, scale: float, row: int, head: int, lib=None) -> 
     if n < 0:
         raise RuntimeError("oracle failed (bad row/head?)")
     return out[:n].copy()
+
+
+def _as_f32_any(x, ndim: int) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.float32)
+    if a.ndim != ndim:
+        raise ValueError(f"expected {ndim} dimensions, got {a.ndim}")
+    return a
+
+
+def qkv_prologue(qkv, n_heads: int, n_kv_heads: int, cos=None, sin=None, q_weight=None, k_weight=None,
+                 eps: float = 1e-6, lib=None):
+    """Split a packed projection output ``qkv`` ``[T, (H + 2*Hkv) * D]`` into float64
+    ``q [T, H, D]``, ``k [T, Hkv, D]``, ``v [T, Hkv, D]``: Q and K optionally RMS-normalised
+    per head (gains ``q_weight``, ``k_weight`` ``[D]``, eps inside the square root) and then
+    rotated with the ``cos``/``sin`` tables ``[T, D]`` (rotate_half pairing); V copied."""
+    lib = lib or load()
+    x = _as_f32_any(qkv, 2)
+    t, width = x.shape
+    if (cos is None) != (sin is None) or (q_weight is None) != (k_weight is None):
+        raise ValueError("give both tables or neither, and both gains or neither")
+    if width % (n_heads + 2 * n_kv_heads) != 0:
+        raise ValueError("qkv width must be (H + 2*Hkv) * D")
+    d = width // (n_heads + 2 * n_kv_heads)
+    cs = _as_f32_any(cos, 2) if cos is not None else None
+    sn = _as_f32_any(sin, 2) if sin is not None else None
+    if cs is not None and (cs.shape != (t, d) or sn.shape != (t, d)):
+        raise ValueError("cos and sin must be [T, D]")
+    qw = _as_f32_any(q_weight, 1) if q_weight is not None else None
+    kw = _as_f32_any(k_weight, 1) if k_weight is not None else None
+    if qw is not None and (qw.shape != (d,) or kw.shape != (d,)):
+        raise ValueError("gains must be [D]")
+    q = np.zeros((t, n_heads, d), np.float64)
+    k = np.zeros((t, n_kv_heads, d), np.float64)
+    v = np.zeros((t, n_kv_heads, d), np.float64)
+    nul = ctypes.POINTER(ctypes.c_float)()
+    p = lambda a: _ptr(a, ctypes.c_float) if a is not None else nul
+    rc = lib.vitattn_ref_qkv_prologue_f64(_ptr(x, ctypes.c_float), p(cs), p(sn), p(qw), p(kw), float(eps),
+                                          _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                          _ptr(v, ctypes.c_double), t, n_heads, n_kv_heads, d)
+    if rc != 0:
+        raise RuntimeError("oracle prologue failed (bad arguments?)")
+    return q, k, v
 
 
 def threads() -> int:

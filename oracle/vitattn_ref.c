@@ -267,3 +267,76 @@ int64_t vitattn_ref_row_probs_f64(const float* q, const float* k, const int32_t*
   for (int64_t j = a; j < b; ++j) p_out[j - a] /= z;
   return b - a;
 }
+
+/* ------------------------------------------------------------------------
+ * The input side of the path: split the packed projection output into Q, K
+ * and V, optionally normalise Q and K per head (RMS), and apply the rope.
+ *
+ * Sources (pages as titled in the reference collection):
+ *  - "inferencelayer 0.2.1 src/vision_gpu.rs", VIS_QKV_ROPE and its doc: a
+ *    packed row holds the query heads, then the key heads, then the value
+ *    heads, each head_dim wide; Q and K are rotated with per-token cos/sin
+ *    tables [tokens, head_dim] computed by the caller, V is copied; the
+ *    rotation is out[d] = x[d] cos[d] + rotate_half(x)[d] sin[d] with
+ *    rotate_half(x)[d] = -x[d + D/2] for d < D/2 and x[d - D/2] otherwise.
+ *  - same page, GLM_QKV_QKNORM_ROPE: a per-head RMS norm of Q and of K over
+ *    head_dim, before the rope, with a [head_dim] gain for each.
+ *  - "hf2q src/inference/vision/vit_gpu.rs", doc of vit_rms_norm_gpu and
+ *    vit_per_head_rms_norm_gpu: y = x / sqrt(mean(x^2) + eps) * gain, eps
+ *    inside the square root, the gain shared by all heads.
+ * Readings: with n_kv_heads < n_heads the packed row is Q heads, then
+ * n_kv_heads K heads, then n_kv_heads V heads (the grouped-query layout the
+ * attention reads); null tables mean no rope, null gains mean no norm.
+ *
+ * qkv : [T, (H + 2 Hkv) * D] values (float32; exact for 16-bit data).
+ * cosv, sinv : [T, D] or both NULL.  qw, kw : [D] or both NULL.
+ * q : [T, H, D], k and v : [T, Hkv, D], float64.
+ * Returns 0, or -1 on a bad argument.
+ * ------------------------------------------------------------------------ */
+static void ref_norm_rope(const float* x, const float* cosr, const float* sinr, const float* w,
+                          double eps, int32_t D, double* out) {
+  double y[1024];
+  for (int32_t d = 0; d < D; ++d) y[d] = (double)x[d];
+  if (w) {
+    double ms = 0.0;
+    for (int32_t d = 0; d < D; ++d) ms += y[d] * y[d];
+    ms /= (double)D;
+    const double r = 1.0 / sqrt(ms + eps);
+    for (int32_t d = 0; d < D; ++d) y[d] = y[d] * r * (double)w[d];
+  }
+  if (cosr) {
+    const int32_t h = D / 2;
+    for (int32_t d = 0; d < D; ++d) {
+      const double rot = d < h ? -y[d + h] : y[d - h];
+      out[d] = y[d] * (double)cosr[d] + rot * (double)sinr[d];
+    }
+  } else {
+    for (int32_t d = 0; d < D; ++d) out[d] = y[d];
+  }
+}
+
+int vitattn_ref_qkv_prologue_f64(const float* qkv, const float* cosv, const float* sinv,
+                                 const float* qw, const float* kw, double eps,
+                                 double* q, double* k, double* v, int32_t n_tokens,
+                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim) {
+  if (n_tokens < 0 || n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return -1;
+  if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 1024) return -1;
+  if ((cosv == NULL) != (sinv == NULL) || (qw == NULL) != (kw == NULL)) return -1;
+  if (qw && !(eps >= 0.0)) return -1;
+  if (n_tokens == 0) return 0;
+  if (!qkv || !q || !k || !v) return -1;
+  const int64_t D = head_dim, H = n_heads, G = n_kv_heads;
+  const int64_t row_len = (H + 2 * G) * D;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    const float* row = qkv + t * row_len;
+    const float* c = cosv ? cosv + t * D : NULL;
+    const float* s = sinv ? sinv + t * D : NULL;
+    for (int64_t h = 0; h < H; ++h) ref_norm_rope(row + h * D, c, s, qw, eps, head_dim, q + (t * H + h) * D);
+    for (int64_t h = 0; h < G; ++h) {
+      ref_norm_rope(row + (H + h) * D, c, s, kw, eps, head_dim, k + (t * G + h) * D);
+      for (int64_t d = 0; d < D; ++d) v[(t * G + h) * D + d] = (double)row[(H + G + h) * D + d];
+    }
+  }
+  return 0;
+}

@@ -335,6 +335,110 @@ def pin_masked_rows_match_full(lib):
         assert np.array_equal(got, full[rows])
 
 
+# ---- the input side: qkv split, per-head RMS norm, rope ("inferencelayer 0.2.1
+# src/vision_gpu.rs", VIS_QKV_ROPE and GLM_QKV_QKNORM_ROPE; "hf2q ... vit_gpu.rs",
+# vit_rms_norm_gpu: eps inside the square root)
+
+def _packed(t, h, g, d, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((t, (h + 2 * g) * d)) * std).astype(np.float32), rng
+
+
+def pin_prologue_split_is_exact(lib):
+    # no tables and no gains: Q, K and V are the packed row's head slots, bit for bit
+    for h, g in ((4, 4), (6, 2), (3, 1)):
+        x, _ = _packed(5, h, g, 8, seed=60 + h)
+        q, k, v = oracle.qkv_prologue(x, h, g, lib=lib)
+        assert np.array_equal(q, x[:, :h * 8].reshape(5, h, 8).astype(np.float64))
+        assert np.array_equal(k, x[:, h * 8:(h + g) * 8].reshape(5, g, 8).astype(np.float64))
+        assert np.array_equal(v, x[:, (h + g) * 8:].reshape(5, g, 8).astype(np.float64))
+
+
+def pin_prologue_rope_quarter_turn(lib):
+    # cos = 1, sin = 0 is the identity; cos = 0, sin = 1 is rotate_half itself: the low half
+    # takes minus the high half, the high half takes the low half (values exact)
+    x, _ = _packed(3, 2, 1, 8, seed=62)
+    one, zero = np.ones((3, 8), np.float32), np.zeros((3, 8), np.float32)
+    q, k, v = oracle.qkv_prologue(x, 2, 1, cos=one, sin=zero, lib=lib)
+    assert np.array_equal(q, x[:, :16].reshape(3, 2, 8).astype(np.float64))
+    q, k, v = oracle.qkv_prologue(x, 2, 1, cos=zero, sin=one, lib=lib)
+    xq = x[:, :16].reshape(3, 2, 8).astype(np.float64)
+    assert np.array_equal(q[..., :4], -xq[..., 4:]) and np.array_equal(q[..., 4:], xq[..., :4])
+    xk = x[:, 16:24].reshape(3, 1, 8).astype(np.float64)
+    assert np.array_equal(k[..., :4], -xk[..., 4:]) and np.array_equal(k[..., 4:], xk[..., :4])
+    assert np.array_equal(v, x[:, 24:].reshape(3, 1, 8).astype(np.float64))  # V is never rotated
+
+
+def _angle_tables(t, d, seed):
+    # standard rope tables: the angle of dim j equals that of dim j + d/2
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(-4, 4, size=(t, d // 2))
+    ang = np.concatenate([ang, ang], axis=1)
+    return ang, np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def pin_prologue_rope_is_a_rotation(lib):
+    # with tables of one angle per pair (j, j + d/2) the rope rotates each pair: norms are
+    # kept, and dot products of two rotated rows depend only on the angle difference
+    t, h, d = 6, 2, 16
+    x, _ = _packed(t, h, h, d, seed=63)
+    ang, c, s_ = _angle_tables(t, d, 64)
+    q, k, _ = oracle.qkv_prologue(x, h, h, cos=c, sin=s_, lib=lib)
+    q0 = x[:, :h * d].reshape(t, h, d).astype(np.float64)
+    assert np.allclose(np.linalg.norm(q, axis=-1), np.linalg.norm(q0, axis=-1), rtol=1e-6, atol=0)
+    # rotating rows i and j by their angles gives the same dot product as rotating row i by
+    # the difference alone (tables recomputed in float64 and rounded like the others)
+    i, j = 1, 4
+    diff = ang[i] - ang[j]
+    c2, s2 = np.cos(diff).astype(np.float32)[None], np.sin(diff).astype(np.float32)[None]
+    qi, _, _ = oracle.qkv_prologue(x[i:i + 1], h, h, cos=c2, sin=s2, lib=lib)
+    kj = x[j:j + 1, h * d:2 * h * d].reshape(1, h, d).astype(np.float64)
+    lhs = np.sum(q[i] * k[j], axis=-1)
+    rhs = np.sum(qi[0] * kj[0], axis=-1)
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-5)
+
+
+def pin_prologue_rms_norm_closed_form(lib):
+    # a constant head vector c: mean of squares c^2, so y = c / sqrt(c^2 + eps) * gain
+    t, h, d, eps = 2, 2, 8, 0.5
+    x = np.full((t, 3 * h * d), 1.5, np.float32)  # H = Hkv = h: width (h + 2h) d
+    w = np.arange(1, d + 1, dtype=np.float32)
+    q, k, v = oracle.qkv_prologue(x, h, h, q_weight=w, k_weight=2 * w, eps=eps, lib=lib)
+    assert np.allclose(q, 1.5 / np.sqrt(2.25 + eps) * w, rtol=1e-14, atol=0)
+    assert np.allclose(k, 1.5 / np.sqrt(2.25 + eps) * 2 * w, rtol=1e-14, atol=0)
+    assert np.array_equal(v, np.full_like(v, 1.5))
+
+
+def pin_prologue_rms_norm_torch(lib):
+    # PyTorch's rms_norm (float64) per head, with a gain and eps = 0.1
+    import torch
+    import torch.nn.functional as F
+    t, h, g, d = 7, 4, 2, 16
+    x, rng = _packed(t, h, g, d, seed=65, std=2.0)
+    qw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    kw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    q, k, _ = oracle.qkv_prologue(x, h, g, q_weight=qw, k_weight=kw, eps=0.1, lib=lib)
+    xt = torch.from_numpy(x.astype(np.float64))
+    rq = F.rms_norm(xt[:, :h * d].reshape(t, h, d), (d,), torch.from_numpy(qw.astype(np.float64)), 0.1)
+    rk = F.rms_norm(xt[:, h * d:(h + g) * d].reshape(t, g, d), (d,), torch.from_numpy(kw.astype(np.float64)), 0.1)
+    assert np.allclose(q, rq.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(k, rk.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def pin_prologue_norm_then_rope(lib):
+    # the norm comes first: norm + rope equals the rope applied (as a second call, with no
+    # gains) to the normed rows; with a non-uniform gain the other order differs
+    t, h, d = 4, 2, 16
+    x, rng = _packed(t, h, h, d, seed=66)
+    _, c, s_ = _angle_tables(t, d, 67)
+    w = rng.uniform(0.2, 2.0, d).astype(np.float32)
+    q, k, _ = oracle.qkv_prologue(x, h, h, cos=c, sin=s_, q_weight=w, k_weight=w, eps=1e-3, lib=lib)
+    qn, kn, vn = oracle.qkv_prologue(x, h, h, q_weight=w, k_weight=w, eps=1e-3, lib=lib)
+    packed = np.concatenate([qn.reshape(t, -1), kn.reshape(t, -1), vn.reshape(t, -1)], axis=1)
+    q2, k2, _ = oracle.qkv_prologue(packed.astype(np.float32), h, h, cos=c, sin=s_, lib=lib)
+    assert np.allclose(q, q2, rtol=1e-6, atol=1e-6) and np.allclose(k, k2, rtol=1e-6, atol=1e-6)
+
+
 PINS = [
     pin_golden, pin_scale_one_logistic, pin_single_key, pin_constant_v, pin_uniform_when_no_signal,
     pin_weights_are_a_distribution, pin_key_shift_invariance, pin_key_permutation_invariance,
@@ -344,4 +448,6 @@ PINS = [
     pin_causal_torch_sdpa, pin_causal_first_row_is_its_value, pin_window_one_is_identity,
     pin_causal_is_prefix_attention, pin_window_is_band_attention, pin_wide_window_is_no_window,
     pin_masked_rows_match_full,
+    pin_prologue_split_is_exact, pin_prologue_rope_quarter_turn, pin_prologue_rope_is_a_rotation,
+    pin_prologue_rms_norm_closed_form, pin_prologue_rms_norm_torch, pin_prologue_norm_then_rope,
 ]

@@ -55,6 +55,21 @@ MUTANTS = {
     "window-ignored": [("if (window > 0 && (qi - kj >= window", "if (0 && (qi - kj >= window")],
     "window-from-image-start": [("if (window > 0 && (qi - kj >= window || kj - qi >= window)) return 0;",
                                  "if (window > 0 && (kj >= window)) return 0;")],
+    "prologue-rotate-half-sign": [("const double rot = d < h ? -y[d + h] : y[d - h];",
+                                   "const double rot = d < h ? y[d + h] : -y[d - h];")],
+    "prologue-interleaved-pairs": [("const double rot = d < h ? -y[d + h] : y[d - h];",
+                                    "const double rot = d % 2 == 0 ? -y[d + 1] : y[d - 1];")],
+    "prologue-cos-sin-swapped": [("out[d] = y[d] * (double)cosr[d] + rot * (double)sinr[d];",
+                                  "out[d] = y[d] * (double)sinr[d] + rot * (double)cosr[d];")],
+    "prologue-eps-outside-sqrt": [("const double r = 1.0 / sqrt(ms + eps);",
+                                   "const double r = 1.0 / (sqrt(ms) + eps);")],
+    "prologue-sum-not-mean": [("    ms /= (double)D;\n", "")],
+    "prologue-gain-ignored": [("y[d] = y[d] * r * (double)w[d];", "y[d] = y[d] * r;")],
+    "prologue-k-takes-q-gain": [("ref_norm_rope(row + (H + h) * D, c, s, kw,", "ref_norm_rope(row + (H + h) * D, c, s, qw,")],
+    "prologue-v-from-k-slot": [("v[(t * G + h) * D + d] = (double)row[(H + G + h) * D + d];",
+                                "v[(t * G + h) * D + d] = (double)row[(H + h) * D + d];")],
+    "prologue-k-slot-after-q-of-kv-width": [("ref_norm_rope(row + (H + h) * D, c, s, kw,",
+                                            "ref_norm_rope(row + (G + h) * D, c, s, kw,")],
     "value-head-ignored": [("const float* vj = v + j * kv_stride + (int64_t)hk * head_dim;",
                             "const float* vj = v + j * kv_stride;")],
 }

@@ -78,6 +78,41 @@ def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False, cau
     return w, kernel_ms, wall * 1e3 / steps, cfg
 
 
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def time_prologue(name: str, steps: int, warmup: int):
+    """The qkv prologue (split + per-head RMS norm + rope) on the workload's token count and
+    heads; returns (seconds per launch, algorithmic bytes per launch)."""
+    import torch
+
+    import vision_transformer_attention_amd as vta
+    from vision_transformer_attention_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    d = inputs.prologue_inputs(w.lengths, w.n_heads, w.head_dim, w.dtype, seed=w.seed + 100, n_kv_heads=w.n_kv_heads)
+    dev = torch.device("cuda:0")
+    mv = lambda x: x.to(dev) if x is not None else None
+    args = (mv(d["qkv"]), d["n_heads"], d["n_kv_heads"], mv(d["cos"]), mv(d["sin"]), mv(d["q_weight"]),
+            mv(d["k_weight"]))
+    out = vta.qkv_prologue(*args)
+    for _ in range(warmup):
+        vta.qkv_prologue(*args, out=out)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
+    start.record(stream)
+    for _ in range(steps):
+        vta.qkv_prologue(*args, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    sec = start.elapsed_time(end) / steps * 1e-3
+    es = d["qkv"].element_size()
+    t = d["qkv"].shape[0]
+    nbytes = 2 * d["qkv"].numel() * es + 2 * t * w.head_dim * 4 + 2 * w.head_dim * 4
+    return w, sec, nbytes
+
+
 def cpu_baseline(name: str, target_s: float = 12.0):
     """The float64 oracle timed on the host's cores on a bounded sample of query rows."""
     import numpy as np
@@ -146,6 +181,8 @@ def main():
                     help="output element type: the input's, or float32 (16-bit inputs only)")
     ap.add_argument("--causal", action="store_true", help="aligned causal mask inside each image")
     ap.add_argument("--window", type=int, default=0, help="key window |qi - kj| < W (0: none)")
+    ap.add_argument("--prologue", action="store_true",
+                    help="time the qkv prologue (split, per-head RMS norm, rope) instead of the attention")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -158,6 +195,21 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.prologue:
+        w, sec, nbytes = time_prologue(args.workload, args.steps, args.warmup)
+        gbs = nbytes / sec / 1e9
+        log(f"[bench] prologue {args.workload}: {sec * 1e6:.1f} us/launch, {gbs:.0f} GB/s")
+        print(json.dumps({
+            "metric": "qkv prologue GB/s (packed qkv read once, Q/K/V written once, rope tables read once)",
+            "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": w.dtype, "data": "synthetic (seeded N(0,1) projection output, 2-D rope tables)",
+            "config": {"workload": w.name, "tokens": w.total_tokens, "heads": w.n_heads, "kv_heads": w.kv_heads,
+                       "head_dim": w.head_dim, "bytes_per_step": nbytes, "rope": True, "norm": True},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        }), flush=True)
+        return
     log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
     masked = args.causal or args.window > 0
     w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup, args.out_dtype == "f32",

@@ -148,6 +148,48 @@ int vitattn_fwd_masked(const void* q, const void* k, const void* v, void* o,
                        int32_t n_kv_heads, int32_t head_dim, float scale, int32_t causal,
                        int32_t window, int32_t dtype, hipStream_t stream);
 
+/*
+ * vitattn_qkv_prologue -- enqueue the input side of the attention: split the
+ * packed projection output into Q, K and V in the layout vitattn_fwd_gqa
+ * reads, normalise Q and K per head (optional) and apply the rope (optional).
+ * Sources: "inferencelayer 0.2.1 src/vision_gpu.rs", VIS_QKV_ROPE (the
+ * split, rope tables from the caller, V not rotated) and GLM_QKV_QKNORM_ROPE
+ * (the per-head RMS norm of Q and K before the rope); "hf2q
+ * src/inference/vision/vit_gpu.rs", vit_rms_norm_gpu (eps inside the square
+ * root, a [head_dim] gain shared by all heads).
+ *
+ * For every token t, with x a head vector of D = head_dim elements:
+ *   norm (q_weight, k_weight given): x[d] <- x[d] / sqrt(mean(x^2) + eps) * w[d]
+ *   rope (cos_table, sin_table given):
+ *     out[d] = x[d] cos[t,d] + r[d] sin[t,d],  r[d] = -x[d + D/2] (d < D/2),
+ *                                              r[d] =  x[d - D/2] (d >= D/2)
+ * applied to the query heads (gain q_weight) and the key heads (k_weight);
+ * the value heads are copied.  All arithmetic is float32; 16-bit outputs are
+ * rounded to nearest even.
+ *
+ * qkv     : DEVICE, [n_tokens, (n_heads + 2*n_kv_heads) * head_dim] of dtype:
+ *           per token the query heads, then the key heads, then the value
+ *           heads.  16-byte aligned.  Read only.
+ * cos_table, sin_table : DEVICE float32 [n_tokens, head_dim], 16-byte
+ *           aligned, or both NULL (no rope).
+ * q_weight, k_weight : DEVICE float32 [head_dim], 16-byte aligned, or both
+ *           NULL (no norm).  eps : finite, >= 0 (used only with the gains).
+ * q       : DEVICE [n_tokens, n_heads, head_dim] of dtype (written), 16-byte
+ *           aligned.
+ * k, v    : DEVICE [n_tokens, n_kv_heads, head_dim] of dtype (written),
+ *           16-byte aligned.
+ *           The outputs must not overlap qkv or each other.
+ * n_kv_heads : > 0, a divisor of n_heads.  head_dim : 64, 72, 80 or 128.
+ * dtype   : VITATTN_DTYPE_F32, _BF16 or _F16 (inputs and outputs alike;
+ *           others give VITATTN_ERR_UNSUPPORTED_DTYPE).
+ * n_tokens == 0 enqueues nothing.  Validation, asynchrony and error behaviour
+ * are those of vitattn_fwd; no device memory is allocated.
+ */
+int vitattn_qkv_prologue(const void* qkv, const float* cos_table, const float* sin_table,
+                         const float* q_weight, const float* k_weight, float eps, void* q,
+                         void* k, void* v, int32_t n_tokens, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t dtype, hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* vitattn_status_string(int status);
 

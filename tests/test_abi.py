@@ -29,8 +29,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["vitattn_fwd", "vitattn_fwd_gqa", "vitattn_fwd_masked", "vitattn_status_string", "vitattn_last_error",
-         "vitattn_kernel_config"])
+        ["vitattn_fwd", "vitattn_fwd_gqa", "vitattn_fwd_masked", "vitattn_qkv_prologue", "vitattn_status_string",
+         "vitattn_last_error", "vitattn_kernel_config"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -129,6 +129,40 @@ def test_masked_validation_before_any_hip_call(lib, args, status):
     rc = lib.vitattn_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["cu"], a["n_seqs"], a["n_heads"],
                                 a["n_kv_heads"], a["head_dim"], ctypes.c_float(a["scale"]), a["causal"],
                                 a["window"], a["dtype"], None)
+    assert rc == status
+    if status != OK:
+        assert len(lib.vitattn_last_error()) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(n_tokens=-1), INVALID),
+    (dict(n_heads=0), INVALID),
+    (dict(n_kv_heads=3), INVALID),
+    (dict(head_dim=96), BAD_HD),
+    (dict(head_dim=0), BAD_HD),
+    (dict(dtype=3), BAD_DT),            # the prologue writes its input kind: no float32-output codes
+    (dict(dtype=5), BAD_DT),
+    (dict(cos=0), INVALID),             # one rope table without the other
+    (dict(qw=0), INVALID),              # one gain without the other
+    (dict(eps=float("nan")), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(qkv=0), INVALID),
+    (dict(q=FAKE + 4), INVALID),        # 16-byte alignment
+    (dict(v=FAKE + 8), INVALID),
+    (dict(dtype=0, k=FAKE + 8), INVALID),
+    (dict(cos=FAKE + 8, sin=FAKE + 8), INVALID),
+    (dict(cos=0, sin=0, qw=0, kw=0, eps=float("nan"), n_tokens=0), OK),  # no norm: eps unused
+    (dict(n_tokens=0), OK),
+    (dict(n_tokens=0, qkv=0, q=0, k=0, v=0), OK),
+])
+def test_prologue_validation_before_any_hip_call(lib, args, status):
+    a = dict(qkv=FAKE, cos=FAKE, sin=FAKE, qw=FAKE, kw=FAKE, eps=1e-6, q=FAKE, k=FAKE, v=FAKE, n_tokens=4,
+             n_heads=8, n_kv_heads=2, head_dim=80, dtype=1)
+    a.update(args)
+    nul = lambda x: x if x else None
+    rc = lib.vitattn_qkv_prologue(nul(a["qkv"]), nul(a["cos"]), nul(a["sin"]), nul(a["qw"]), nul(a["kw"]),
+                                  ctypes.c_float(a["eps"]), nul(a["q"]), nul(a["k"]), nul(a["v"]), a["n_tokens"],
+                                  a["n_heads"], a["n_kv_heads"], a["head_dim"], a["dtype"], None)
     assert rc == status
     if status != OK:
         assert len(lib.vitattn_last_error()) > 0

@@ -53,6 +53,10 @@ def load_library(path: str | None = None):
     lib.vitattn_fwd_gqa.restype = ctypes.c_int
     lib.vitattn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, i32, i32, vp]
     lib.vitattn_fwd_masked.restype = ctypes.c_int
+    f32p = ctypes.c_void_p
+    lib.vitattn_qkv_prologue.argtypes = [vp, f32p, f32p, f32p, f32p, ctypes.c_float, vp, vp, vp, i32, i32, i32, i32,
+                                         i32, vp]
+    lib.vitattn_qkv_prologue.restype = ctypes.c_int
     lib.vitattn_status_string.argtypes = [ctypes.c_int]
     lib.vitattn_status_string.restype = ctypes.c_char_p
     lib.vitattn_last_error.argtypes = []
@@ -220,3 +224,60 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
             fwd_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_dev.data_ptr(), n_seqs,
                         n_heads, n_kv_heads, head_dim, float(scale), code, stream)
     return out
+
+
+def qkv_prologue(qkv, n_heads: int, n_kv_heads: int | None = None, cos=None, sin=None, q_weight=None,
+                 k_weight=None, eps: float = 1e-6, out=None):
+    """Split the packed projection output into the attention inputs; returns ``(q, k, v)``.
+
+    qkv: contiguous GPU tensor ``[T, (H + 2*Hkv) * D]`` (float32, bfloat16 or float16): per token
+    the query heads, then the key heads, then the value heads.  ``cos``/``sin``: float32
+    ``[T, D]`` rope tables (both or neither); ``q_weight``/``k_weight``: float32 ``[D]`` RMS-norm
+    gains (both or neither; eps inside the square root).  Returns ``q [T, H, D]`` and
+    ``k, v [T, Hkv, D]`` of qkv's dtype (into ``out`` when given), ready for ``fwd``.
+    """
+    import torch
+    lib = load_library()
+    if not isinstance(qkv, torch.Tensor) or qkv.device.type != "cuda" or qkv.dim() != 2 or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous 2-D GPU tensor")
+    code = _dtype_code(qkv)
+    hkv = n_heads if n_kv_heads is None else int(n_kv_heads)
+    if n_heads <= 0 or hkv <= 0 or n_heads % hkv != 0:
+        raise ValueError("n_kv_heads must be a positive divisor of n_heads")
+    t, width = qkv.shape
+    if width % (n_heads + 2 * hkv) != 0:
+        raise ValueError("qkv width must be (n_heads + 2*n_kv_heads) * head_dim")
+    d = width // (n_heads + 2 * hkv)
+    if d not in HEAD_DIMS:
+        raise ValueError(f"head_dim {d} not in {HEAD_DIMS}")
+    if (cos is None) != (sin is None) or (q_weight is None) != (k_weight is None):
+        raise ValueError("give both rope tables or neither, and both gains or neither")
+
+    def f32(x, shape, name):
+        if x is None:
+            return None
+        if (not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.device != qkv.device
+                or tuple(x.shape) != shape or not x.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on qkv's device")
+        return x
+    cos, sin = f32(cos, (t, d), "cos"), f32(sin, (t, d), "sin")
+    q_weight, k_weight = f32(q_weight, (d,), "q_weight"), f32(k_weight, (d,), "k_weight")
+    if not math.isfinite(eps) or eps < 0:
+        raise ValueError("eps must be finite and >= 0")
+    if out is None:
+        out = (torch.empty((t, n_heads, d), dtype=qkv.dtype, device=qkv.device),
+               torch.empty((t, hkv, d), dtype=qkv.dtype, device=qkv.device),
+               torch.empty((t, hkv, d), dtype=qkv.dtype, device=qkv.device))
+    q, k, v = out
+    for x, shape in ((q, (t, n_heads, d)), (k, (t, hkv, d)), (v, (t, hkv, d))):
+        if tuple(x.shape) != shape or x.dtype != qkv.dtype or x.device != qkv.device or not x.is_contiguous():
+            raise ValueError("out must be contiguous (q, k, v) of the prologue's shapes and qkv's dtype")
+    if t == 0:
+        return q, k, v
+    ptr = lambda x: x.data_ptr() if x is not None else None
+    with torch.cuda.device(qkv.device):
+        stream = torch.cuda.current_stream(qkv.device).cuda_stream
+        _check(lib, lib.vitattn_qkv_prologue(qkv.data_ptr(), ptr(cos), ptr(sin), ptr(q_weight), ptr(k_weight),
+                                             ctypes.c_float(eps), q.data_ptr(), k.data_ptr(), v.data_ptr(), t,
+                                             n_heads, hkv, d, code, stream))
+    return q, k, v

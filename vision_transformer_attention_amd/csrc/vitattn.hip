@@ -56,6 +56,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 namespace {
 
@@ -1502,6 +1503,165 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 }
 
 // ----------------------------------------------------------------------------
+// The input side of the path: the packed projection output split into Q, K and V in the
+// layout the attention kernels read, with an optional per-head RMS norm of Q and K and the
+// rope ("inferencelayer 0.2.1 src/vision_gpu.rs", VIS_QKV_ROPE and GLM_QKV_QKNORM_ROPE;
+// "hf2q src/inference/vision/vit_gpu.rs", vit_rms_norm_gpu: y = x / sqrt(mean(x^2) + eps)
+// * gain).  A packed row is [H query heads | Hkv key heads | Hkv value heads] of D elements.
+// HBM-bound: every element is read once and written once, and the cos/sin tables
+// ([tokens, D] float32) are read once per token row.
+//
+// One wavefront per token row: it loads the cos/sin values and the gains of its elements
+// once and reuses them for every head of the row, and walks the row's head vectors (one
+// contiguous run of (H + 2 Hkv) * D elements) a few at a time.  A head vector sits in a group
+// of GS lanes (a power of two), EL elements per lane; EL is 8 (16-byte loads of 16-bit data)
+// where half a head is a whole number of 8-element lanes (D = 64, 80, 128) and 4 otherwise
+// (D = 72).  The rotate_half partner of a lane's elements (element d pairs with d +- D/2) is
+// then the whole EL of the lane D/(2 EL) away, one shuffle per element, and the RMS sum is an
+// xor butterfly inside the group.
+// ----------------------------------------------------------------------------
+constexpr int kF32Elem = 2;  // element kind of float32 data (the 16-bit kinds are kBF16, kF16)
+
+// N (4 or 8) consecutive elements <-> float.  Eight 16-bit elements move as one 16-byte
+// access, marked non-temporal: every byte is touched once, so it need not stay in the caches.
+template <int E, int N>
+struct ElemN {
+  static __device__ __forceinline__ void load(const unsigned char* p, float (&x)[N]) {
+    if constexpr (E != kF32Elem && N == 8) {
+      const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+      if constexpr (E == kBF16) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          x[2 * h] = __uint_as_float(w[h] << 16);
+          x[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+        }
+      } else {  // (the whole vector reinterpreted at once: a per-word bit_cast of w[h] was
+                // compiled as the first word's, repeated)
+        const f16x8_t hv = __builtin_bit_cast(f16x8_t, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)hv[i];
+      }
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < N / 4; ++h) {
+      const unsigned char* ph = p + h * 4 * (E == kF32Elem ? 4 : 2);
+      if constexpr (E == kF32Elem) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(ph);
+        for (int i = 0; i < 4; ++i) x[4 * h + i] = w[i];
+      } else if constexpr (E == kBF16) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(ph);
+        x[4 * h + 0] = __uint_as_float(w[0] << 16);
+        x[4 * h + 1] = __uint_as_float(w[0] & 0xffff0000u);
+        x[4 * h + 2] = __uint_as_float(w[1] << 16);
+        x[4 * h + 3] = __uint_as_float(w[1] & 0xffff0000u);
+      } else {
+        const f16x4_t w = *reinterpret_cast<const f16x4_t*>(ph);
+        for (int i = 0; i < 4; ++i) x[4 * h + i] = (float)w[i];
+      }
+    }
+  }
+  static __device__ __forceinline__ void store(unsigned char* p, const float (&x)[N]) {
+    if constexpr (E != kF32Elem && N == 8) {
+      const u32x4_t w = {cvt_pk<E>(x[0], x[1]), cvt_pk<E>(x[2], x[3]), cvt_pk<E>(x[4], x[5]), cvt_pk<E>(x[6], x[7])};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < N / 4; ++h) {
+      unsigned char* ph = p + h * 4 * (E == kF32Elem ? 4 : 2);
+      if constexpr (E == kF32Elem)
+        *reinterpret_cast<f32x4_t*>(ph) = f32x4_t{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
+      else
+        *reinterpret_cast<u32x2_t*>(ph) =
+            u32x2_t{cvt_pk<E>(x[4 * h], x[4 * h + 1]), cvt_pk<E>(x[4 * h + 2], x[4 * h + 3])};
+    }
+  }
+};
+
+__device__ __forceinline__ void load_f32n(const float* p, float* x, int n) {
+  for (int h = 0; h < n / 4; ++h) {
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(p + 4 * h);
+    for (int i = 0; i < 4; ++i) x[4 * h + i] = w[i];
+  }
+}
+
+constexpr int kPrologueThreads = 256;  // four token rows per workgroup
+
+template <int E, int D>
+__global__ __launch_bounds__(kPrologueThreads) void qkv_prologue_kernel(
+    const unsigned char* __restrict__ qkv, const float* __restrict__ cosv, const float* __restrict__ sinv,
+    const float* __restrict__ qw, const float* __restrict__ kw, float eps, unsigned char* __restrict__ q,
+    unsigned char* __restrict__ k, unsigned char* __restrict__ v, int n_tokens, int n_heads, int n_kv_heads) {
+  constexpr int EL = (D / 2) % 8 == 0 ? 8 : 4;  // elements per lane
+  constexpr int LH = D / EL;                      // lanes holding a head vector
+  constexpr int GS = LH <= 8 ? 8 : (LH <= 16 ? 16 : 32);
+  constexpr int HPI = 64 / GS;  // head vectors per pass of the wavefront
+  constexpr int ES = E == kF32Elem ? 4 : 2;
+  static_assert(D % 8 == 0 && LH <= 32 && (LH % 2) == 0, "halves of a head vector are whole lanes");
+  const int lane = threadIdx.x & 63;
+  const int hg = lane / GS, j = lane % GS;
+  const bool on = j < LH;
+  const int row = blockIdx.x * (kPrologueThreads / 64) + (threadIdx.x >> 6);
+  if (row >= n_tokens) return;  // the whole wavefront; no barrier follows
+  const int nh3 = n_heads + 2 * n_kv_heads;
+  const bool low = j < LH / 2;
+  const int src = (lane & ~(GS - 1)) + (low ? j + LH / 2 : j - LH / 2);  // rope partner lane
+
+  float c[EL], sn[EL], wq[EL], wk[EL];
+  if (cosv && on) {
+    load_f32n(cosv + (size_t)row * D + j * EL, c, EL);
+    load_f32n(sinv + (size_t)row * D + j * EL, sn, EL);
+  }
+  if (qw && on) {
+    load_f32n(qw + j * EL, wq, EL);
+    load_f32n(kw + j * EL, wk, EL);
+  }
+  const unsigned char* in = qkv + (size_t)row * nh3 * D * ES;
+#pragma unroll 4
+  for (int base = 0; base < nh3; base += HPI) {
+    const int slot = base + hg;
+    const bool live = on && slot < nh3;
+    const bool is_q = slot < n_heads, is_v = slot >= n_heads + n_kv_heads;
+    float x[EL];
+#pragma unroll
+    for (int i = 0; i < EL; ++i) x[i] = 0.f;
+    if (live) ElemN<E, EL>::load(in + ((size_t)slot * D + j * EL) * ES, x);
+    if (qw) {  // per-head RMS norm of Q and K
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < EL; ++i) ss += x[i] * x[i];
+#pragma unroll
+      for (int m = 1; m < GS; m <<= 1) ss += __shfl_xor(ss, m);
+      if (!is_v) {
+        const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+        for (int i = 0; i < EL; ++i) x[i] = x[i] * r * (is_q ? wq[i] : wk[i]);
+      }
+    }
+    if (cosv) {  // rope: x[d] cos[d] + rotate_half(x)[d] sin[d]
+      float pr[EL];
+#pragma unroll
+      for (int i = 0; i < EL; ++i) pr[i] = __shfl(x[i], src);
+      if (!is_v) {
+#pragma unroll
+        for (int i = 0; i < EL; ++i) x[i] = x[i] * c[i] + (low ? -pr[i] : pr[i]) * sn[i];
+      }
+    }
+    if (live) {
+      unsigned char* dst;
+      if (is_q)
+        dst = q + (((size_t)row * n_heads + slot) * D + j * EL) * ES;
+      else if (!is_v)
+        dst = k + (((size_t)row * n_kv_heads + (slot - n_heads)) * D + j * EL) * ES;
+      else
+        dst = v + (((size_t)row * n_kv_heads + (slot - n_heads - n_kv_heads)) * D + j * EL) * ES;
+      ElemN<E, EL>::store(dst, x);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Host side.
 // ----------------------------------------------------------------------------
 thread_local char g_last_error[512] = "";
@@ -1712,6 +1872,26 @@ int validate(int32_t head_dim, int32_t dtype) {
   return VITATTN_OK;
 }
 
+// The prologue launch: kernel by (element kind, head_dim).
+const void* prologue_kernel(int32_t dtype, int32_t head_dim) {
+  auto pick = [&](auto e) -> const void* {
+    constexpr int E = decltype(e)::value;
+    switch (head_dim) {
+      case 64: return reinterpret_cast<const void*>(&qkv_prologue_kernel<E, 64>);
+      case 72: return reinterpret_cast<const void*>(&qkv_prologue_kernel<E, 72>);
+      case 80: return reinterpret_cast<const void*>(&qkv_prologue_kernel<E, 80>);
+      case 128: return reinterpret_cast<const void*>(&qkv_prologue_kernel<E, 128>);
+      default: return nullptr;
+    }
+  };
+  switch (dtype) {
+    case VITATTN_DTYPE_F32: return pick(std::integral_constant<int, kF32Elem>{});
+    case VITATTN_DTYPE_BF16: return pick(std::integral_constant<int, kBF16>{});
+    case VITATTN_DTYPE_F16: return pick(std::integral_constant<int, kF16>{});
+    default: return nullptr;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -1817,6 +1997,51 @@ int vitattn_fwd_gqa(const void* q, const void* k, const void* v, void* o, const 
 int vitattn_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t n_seqs,
                 int32_t n_heads, int32_t head_dim, float scale, int32_t dtype, hipStream_t stream) {
   return vitattn_fwd_gqa(q, k, v, o, cu_seqlens, n_seqs, n_heads, n_heads, head_dim, scale, dtype, stream);
+}
+
+int vitattn_qkv_prologue(const void* qkv, const float* cos_table, const float* sin_table, const float* q_weight,
+                         const float* k_weight, float eps, void* q, void* k, void* v, int32_t n_tokens,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (n_tokens < 0) return fail(VITATTN_ERR_INVALID_ARG, "n_tokens must be >= 0 (got %d)", n_tokens);
+  if (n_heads <= 0) return fail(VITATTN_ERR_INVALID_ARG, "n_heads must be > 0 (got %d)", n_heads);
+  if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
+    return fail(VITATTN_ERR_INVALID_ARG, "n_kv_heads must be a positive divisor of n_heads (got %d for %d heads)",
+                n_kv_heads, n_heads);
+  if (dtype != VITATTN_DTYPE_F32 && dtype != VITATTN_DTYPE_BF16 && dtype != VITATTN_DTYPE_F16)
+    return fail(VITATTN_ERR_UNSUPPORTED_DTYPE, "the prologue takes dtype F32, BF16 or F16 (got %d)", dtype);
+  const void* func = prologue_kernel(dtype, head_dim);
+  if (!func) return fail(VITATTN_ERR_UNSUPPORTED_HEAD_DIM, "head_dim %d not in {64, 72, 80, 128}", head_dim);
+  if ((cos_table == nullptr) != (sin_table == nullptr))
+    return fail(VITATTN_ERR_INVALID_ARG, "give both rope tables or neither");
+  if ((q_weight == nullptr) != (k_weight == nullptr))
+    return fail(VITATTN_ERR_INVALID_ARG, "give both norm gains or neither");
+  if (q_weight && !(std::isfinite(eps) && eps >= 0.0f)) return fail(VITATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (n_tokens == 0) return VITATTN_OK;
+  if (!qkv || !q || !k || !v) return fail(VITATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (((uintptr_t)qkv | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15u)
+    return fail(VITATTN_ERR_INVALID_ARG, "qkv, q, k and v must be 16-byte aligned");
+  if (((uintptr_t)cos_table | (uintptr_t)sin_table | (uintptr_t)q_weight | (uintptr_t)k_weight) & 15u)
+    return fail(VITATTN_ERR_INVALID_ARG, "the rope tables and norm gains must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  int rc = get_device_state(&st);
+  if (rc != VITATTN_OK) return rc;
+  if ((long long)n_tokens * (n_heads + 2LL * n_kv_heads) * head_dim >= (1LL << 40))
+    return fail(VITATTN_ERR_INVALID_ARG, "qkv too large");
+  const long long blocks = ((long long)n_tokens + kPrologueThreads / 64 - 1) / (kPrologueThreads / 64);
+  const unsigned char* a0 = static_cast<const unsigned char*>(qkv);
+  unsigned char *a1 = static_cast<unsigned char*>(q), *a2 = static_cast<unsigned char*>(k),
+                *a3 = static_cast<unsigned char*>(v);
+  int nh = n_heads, nkv = n_kv_heads;
+  int nt = n_tokens;
+  void* args[] = {&a0, (void*)&cos_table, (void*)&sin_table, (void*)&q_weight, (void*)&k_weight, &eps,
+                  &a1, &a2, &a3, &nt, &nh, &nkv};
+  (void)hipGetLastError();
+  hipError_t e = hipLaunchKernel(func, dim3((unsigned)blocks), dim3(kPrologueThreads), args, 0, stream);
+  if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "prologue launch: %s", hipGetErrorString(e));
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(VITATTN_ERR_HIP, "after prologue launch: %s", hipGetErrorString(e));
+  return VITATTN_OK;
 }
 
 }  // extern "C"

@@ -137,3 +137,54 @@ def make(w: Workload | str):
     qt, kt, vt = (torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
     cu = torch.from_numpy(w.cu_seqlens())
     return qt, kt, vt, cu, w.softmax_scale
+
+
+def prologue_inputs(lengths, n_heads: int, head_dim: int, dtype: str = BF16, seed: int = 0,
+                    n_kv_heads: int | None = None, rope: bool = True, norm: bool = True,
+                    theta: float = 100.0):
+    """Seeded inputs of the qkv prologue: a dict with ``qkv`` (torch, ``[T, (H + 2*Hkv) * D]``
+    in ``dtype``), ``cos``/``sin`` (float32 ``[T, D]`` or None), ``q_weight``/``k_weight``
+    (float32 ``[D]`` or None), ``cu_seqlens`` and the head counts.
+
+    Recipe: ``default_rng(seed)`` draws the packed projection output as float32
+    ``standard_normal`` (rounded to the 16-bit kinds by torch), then the two gains uniform in
+    [0.5, 1.5].  The rope tables follow each image's 2-D patch grid (width ceil(sqrt(L)),
+    patch i at row i // width, column i % width): of the D/2 rotated pairs, the first half
+    turn with the row and the second half with the column, pair j of a half at frequency
+    theta^(-j / (D/4)).  The angle of element d equals that of d + D/2 (the rotate_half
+    pairing)."""
+    import torch
+    hkv = n_heads if n_kv_heads is None else int(n_kv_heads)
+    t = int(sum(lengths))
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((t, (n_heads + 2 * hkv) * head_dim), dtype=np.float32)
+    qw = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    kw = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    half, quarter = head_dim // 2, head_dim // 4
+    ang = np.zeros((t, half), np.float64)
+    pos = 0
+    for n in lengths:
+        n = int(n)
+        if n == 0:
+            continue
+        width = int(math.ceil(math.sqrt(n)))
+        i = np.arange(n)
+        r, c = (i // width).astype(np.float64), (i % width).astype(np.float64)
+        f_row = theta ** (-np.arange(quarter) / quarter)
+        f_col = theta ** (-np.arange(half - quarter) / max(half - quarter, 1))
+        ang[pos:pos + n, :quarter] = r[:, None] * f_row[None, :]
+        ang[pos:pos + n, quarter:] = c[:, None] * f_col[None, :]
+        pos += n
+    ang = np.concatenate([ang, ang], axis=1)
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[dtype]
+    return {
+        "qkv": torch.from_numpy(x).to(tdt),
+        "cos": torch.from_numpy(np.cos(ang).astype(np.float32)) if rope else None,
+        "sin": torch.from_numpy(np.sin(ang).astype(np.float32)) if rope else None,
+        "q_weight": torch.from_numpy(qw) if norm else None,
+        "k_weight": torch.from_numpy(kw) if norm else None,
+        "cu_seqlens": torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)),
+        "n_heads": int(n_heads),
+        "n_kv_heads": hkv,
+        "head_dim": int(head_dim),
+    }

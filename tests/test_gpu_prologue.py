@@ -96,21 +96,24 @@ def test_prologue_full_packed_batch_and_out_buffers():
         assert float(excess.max()) <= 0.0
 
 
+@pytest.mark.parametrize("dtype,head_dim", [(inputs.BF16, 80), (inputs.F16, 72), (inputs.F32, 64)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_prologue_then_attention(causal):
+def test_prologue_then_attention(causal, dtype, head_dim):
     # the whole path: the prologue and the attention on the GPU against the oracle's prologue
-    # (its outputs rounded to bf16, as the GPU's are) and the oracle's attention
+    # (its outputs rounded to the element kind, as the GPU's are) and the oracle's attention
     lengths = [257, 64, 1, 130]
-    d = inputs.prologue_inputs(lengths, n_heads=8, head_dim=80, dtype=inputs.BF16, seed=74, n_kv_heads=2)
+    d = inputs.prologue_inputs(lengths, n_heads=8, head_dim=head_dim, dtype=dtype, seed=74, n_kv_heads=2)
     dev = torch.device(DEV)
     mv = lambda x: x.to(dev) if x is not None else None
     q, k, v = vta.qkv_prologue(mv(d["qkv"]), 8, 2, mv(d["cos"]), mv(d["sin"]), mv(d["q_weight"]),
                                mv(d["k_weight"]), eps=1e-6)
     cu = d["cu_seqlens"]
-    o = vta.fwd(q, k, v, cu.to(dev), 80 ** -0.5, causal=causal).cpu()
+    scale = head_dim ** -0.5
+    o = vta.fwd(q, k, v, cu.to(dev), scale, causal=causal).cpu()
     rq, rk, rv = oracle.qkv_prologue(d["qkv"], 8, 2, d["cos"], d["sin"], d["q_weight"], d["k_weight"], eps=1e-6)
-    b = lambda a: torch.from_numpy(a).to(torch.bfloat16)
-    ref = oracle.attention(b(rq), b(rk), b(rv), cu, 80 ** -0.5, causal=causal)
+    kind = {inputs.BF16: torch.bfloat16, inputs.F16: torch.float16, inputs.F32: torch.float32}[dtype]
+    b = lambda a: torch.from_numpy(a).to(kind)
+    ref = oracle.attention(b(rq), b(rk), b(rv), cu, scale, causal=causal)
     err, where = max_abs_err(o, ref)
-    say(f"[prologue] prologue + attention causal={causal}: max-abs err {err:.3e} at {where}")
-    assert err <= TOL[inputs.BF16]
+    say(f"[prologue] prologue + attention {dtype} D={head_dim} causal={causal}: max-abs err {err:.3e} at {where}")
+    assert err <= TOL[dtype]

@@ -134,6 +134,12 @@ def cpu_baseline(name: str, target_s: float = 12.0):
         oracle.attention_rows(q, k, v, cu, scale, rows)
         return time.perf_counter() - t0, flops, n_rows
 
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     dt, fl, n = run(16)
     per_row = max(dt / n, 1e-6)
     n_rows = int(min(w.total_tokens, max(16, target_s / per_row)))
@@ -142,9 +148,10 @@ def cpu_baseline(name: str, target_s: float = 12.0):
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
+        "cpu_model": model,
         "kind": "oracle",
-        "sample": f"{n} of {w.total_tokens} query rows of {name} (all 16 heads, every key of each row's image), "
-                  f"float64, {dt:.1f} s",
+        "sample": f"{n} of {w.total_tokens} query rows of {name} (all {w.n_heads} heads, every key of each row's "
+                  f"image), float64, {dt:.1f} s",
     }
 
 
@@ -259,6 +266,7 @@ def main():
             "workload": w.name, "lengths": list(w.lengths), "tokens": w.total_tokens, "heads": w.n_heads,
             "head_dim": w.head_dim, "kv_heads": w.kv_heads, "out_dtype": "f32" if args.out_dtype == "f32" else w.dtype,
             "causal": bool(args.causal), "window": args.window,
+            "caches": "warm: inputs resident in HBM, launches back to back on one stream",
             "flops_per_step": flops, "block_m": None if masked else cfg["block_m"],
             "block_n": cfg["block_n"], "waves_per_workgroup": cfg["waves"], "grid": cfg["grid"],
         },

@@ -1047,6 +1047,20 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   else
     Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
 
+  if (row0 >= qend) {
+    // No row of this wavefront lies in the sequence (the last, partial item of an image): it
+    // keeps only its share of the DMA and the barriers, so that the SIMD time goes to the
+    // other workgroup on the CU.  The same barriers as below, one per tile.
+    for (int t = 0; t < ntiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 1 < ntiles)
+        Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN,
+                                      item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+    }
+    return;
+  }
+
   bf16x8_t Q[C::QB][C::NK32];
   s16x4_t QT[C::QB];
   load_q16<C>(Q, QT, q, row0, qend, item.head, n_heads, negate, lane);

@@ -142,6 +142,32 @@ def test_non_default_stream_and_no_host_sync_needed():
     assert err <= TOL[inputs.BF16]
 
 
+def test_concurrent_streams_match_sequential_bitwise():
+    # launches on two streams at once (no host sync between them) give the results of the
+    # same launches one after the other: the library keeps no per-call state on the device
+    import vision_transformer_attention_amd as vta
+    dev = torch.device("cuda:0")
+    cases = []
+    for w, kw in ((inputs.WORKLOADS["page-912"], {}), (inputs.custom([700, 64, 1, 300], n_heads=8, head_dim=64,
+                                                                      dtype=inputs.BF16, seed=17, n_kv_heads=2),
+                                                       {"causal": True})):
+        q, k, v, cu, scale = inputs.make(w)
+        cases.append(([x.to(dev) for x in (q, k, v, cu)], scale, kw))
+    seq = []
+    for (q, k, v, cu), scale, kw in cases:
+        seq.append(vta.fwd(q, k, v, cu, scale, **kw))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(c[0][0]) for c in cases]
+    for _ in range(20):  # many launches in flight on both streams
+        for st, ((q, k, v, cu), scale, kw), o in zip(streams, cases, outs):
+            with torch.cuda.stream(st):
+                vta.fwd(q, k, v, cu, scale, out=o, check_cu=False, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(seq, outs):
+        assert torch.equal(a, b)
+
+
 def test_constant_v_gives_constant_output():
     w = inputs.custom([1000], n_heads=2, head_dim=80, dtype=inputs.BF16, seed=16)
     q, k, v, cu, scale = inputs.make(w)

@@ -115,7 +115,8 @@ def test_deterministic_bitwise(name):
     # The launch has a fixed schedule (no atomics, no order-dependent reductions), so any
     # run-to-run difference means a race: an LDS buffer reused too early, or a register
     # overwritten while an in-flight matrix instruction still reads it.  page-912 runs the
-    # 64-query items, packed-varlen-8 the 256-query ones.
+    # short-image items split by keys between wavefront pairs, packed-varlen-8 the 256-query
+    # ones.
     if name == "f32-mixed":
         w = inputs.custom([700, 300, 45], n_heads=4, head_dim=80, dtype=inputs.F32, seed=31)
     else:

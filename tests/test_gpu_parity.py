@@ -79,6 +79,37 @@ def test_many_sequences_unsorted_and_split_launches():
     check_workload(w, full=True)
 
 
+@pytest.mark.parametrize("head_dim", [80, 128])
+def test_one_image_at_an_offset_through_the_raw_abi(head_dim):
+    # A launch over one image takes a closed-form plan; its rows [a, b) need not start at row
+    # 0 of the buffers (cu_seqlens[0] is the image's first row).  Rows outside the image, and
+    # every row of a launch over one empty image, keep what the output held.
+    from vision_transformer_attention_amd import binding
+    t, a, b = 300, 37, 237
+    w = inputs.custom([t], n_heads=3, head_dim=head_dim, dtype=inputs.BF16, seed=15)
+    q, k, v, _cu, scale = inputs.make(w)
+    d = torch.device("cuda:0")
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    sentinel = torch.full_like(qd, 7.0)
+    for lo, hi in ((a, b), (100, 100), (a, a + 1)):
+        say(f"one image rows [{lo}, {hi}) of {t}, head_dim {head_dim}")
+        o = sentinel.clone()
+        cu = torch.tensor([lo, hi], dtype=torch.int32, device=d)
+        binding.fwd_raw(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), cu.data_ptr(), 1, 3, head_dim,
+                        scale, binding.DTYPE_BF16, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        o = o.cpu()
+        assert torch.equal(o[:lo], sentinel[:lo].cpu()) and torch.equal(o[hi:], sentinel[hi:].cpu())
+        if hi > lo:
+            alone = run_gpu(q[lo:hi].contiguous(), k[lo:hi].contiguous(), v[lo:hi].contiguous(),
+                            torch.tensor([0, hi - lo], dtype=torch.int32), scale)
+            assert torch.equal(o[lo:hi], alone)  # the same launch on its own buffers
+            ref = oracle.attention(q[lo:hi], k[lo:hi], v[lo:hi], torch.tensor([0, hi - lo], dtype=torch.int32),
+                                   scale)
+            err = float(np.max(np.abs(o[lo:hi].float().numpy().astype(np.float64) - ref)))
+            assert err <= TOL[inputs.BF16], err
+
+
 def test_empty_batch_is_a_noop():
     d = torch.device("cuda:0")
     q = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=d)

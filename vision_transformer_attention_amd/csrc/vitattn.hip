@@ -26,7 +26,9 @@
 //    Slots are assigned so that the workgroups of one XCD (blockIdx % 8) take
 //    consecutive items, which share a (sequence, head) and so its K/V in that
 //    XCD's L2.  When the large query tiles would leave most of the grid idle (one
-//    short image), the launch re-plans with small ones.
+//    short image), the launch re-plans with small ones, and an unmasked launch whose
+//    small items are still too few splits each item's keys between two wavefronts
+//    whose partial results are merged through LDS.
 //  * Scores are computed transposed, S^T = K.Q^T, with v_mfma_f32_16x16x32_bf16
 //    (float32: v_mfma_f32_16x16x4_f32).  In that accumulator layout a lane holds
 //    4 keys of one query, so a row max is in-lane plus two cross-lane steps, and
@@ -1221,13 +1223,13 @@ __device__ __forceinline__ void run_item_split(const Item& item, const __bf16* _
 // Masked attention (aligned causal and/or a key window; mask rules at key_visible).
 //
 // An item's keys narrow to [klo, khi), the keys some of its queries see
-// (mask_key_range), covered as in run_item by tiles that end at khi.  Each wavefront
-// classifies each 32-key step against its own query rows: no key seen by any row (the
-// step is skipped), every key seen by every row (the unmasked step, once every row has an
-// exponent offset), or partial.  A partial step masks element by element, and a row may
-// have no offset yet (negM = +inf: none of its keys so far was visible); such a row takes
-// its offset from the first step in which it sees a key, exactly as the first step of an
-// unmasked item does.
+// (mask_key_range), covered as in run_item by tiles that end at khi.  For its own query
+// rows each wavefront finds the run of tiles whose every key all of its rows see; that
+// run takes the unmasked tile body, and the tiles before and after it go 32 keys at a
+// time: a step that no row sees is skipped, any other goes through step_32_masked, which
+// applies per row a lower and an upper key bound.  A row may have no offset yet (negM =
+// +inf: none of its keys so far was visible); such a row takes its offset from the first
+// step in which it sees a key, exactly as the first step of an unmasked item does.
 // ----------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void step_32_masked(const __bf16* Ks, const __bf16* Vs, int kb0, int key_s,
@@ -1449,22 +1451,46 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   lds_u8_t* stage = (lds_u8_t*)smem + ((sizeof(PlanLds) + 15) / 16) * 16;
 
   const int G = gridDim.x;
-  plan_load<CA::NT>(plan, cu, n_seqs);
-  int n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CA::BM);
   // Every decision below depends only on cu_seqlens, so every workgroup takes the same.
   // Short images, whose large items would fill less than half of the grid, take CB's small
   // query blocks; unmasked, when even twice as many of those items fit in one round of the
   // grid, each is split further between wavefront pairs by keys (run_item_split).
-  const bool small = 2 * n_items < G;
-  bool split = false;
-  if (small) {
-    __syncthreads();  // everyone has read the item count
-    n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM);
-    if constexpr (!MASK) {
-      split = 2 * n_items <= G;
-      if (split) {
-        __syncthreads();
-        n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM / 2);
+  int n_items;
+  bool small, split = false;
+  if (n_seqs == 1) {
+    // One image: the same plan in closed form, without the ordering and the scans.
+    const int a = cu[0], b = cu[1];
+    auto count = [&](int bm_) { return ceil_div(b - a, bm_) * n_heads; };
+    n_items = count(CA::BM);
+    small = 2 * n_items < G;
+    if (small) {
+      n_items = count(CB::BM);
+      if constexpr (!MASK) {
+        split = 2 * n_items <= G;
+        if (split) n_items = count(CB::BM / 2);
+      }
+    }
+    if (threadIdx.x == 0) {
+      plan.cu[0] = a;
+      plan.cu[1] = b;
+      plan.order[0] = 0;
+      plan.prefix[0] = 0;
+      plan.prefix[1] = n_items;
+    }
+    __syncthreads();
+  } else {
+    plan_load<CA::NT>(plan, cu, n_seqs);
+    n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CA::BM);
+    small = 2 * n_items < G;
+    if (small) {
+      __syncthreads();  // everyone has read the item count
+      n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM);
+      if constexpr (!MASK) {
+        split = 2 * n_items <= G;
+        if (split) {
+          __syncthreads();
+          n_items = plan_items<CA::NT>(plan, n_seqs, n_heads, CB::BM / 2);
+        }
       }
     }
   }

@@ -1658,7 +1658,6 @@ __global__ __launch_bounds__(kPrologueThreads) void qkv_prologue_kernel(
     load_f32n(kw + j * EL, wk, EL);
   }
   const unsigned char* in = qkv + (size_t)row * nh3 * D * ES;
-#pragma unroll 4
   for (int base = 0; base < nh3; base += HPI) {
     const int slot = base + hg;
     const bool live = on && slot < nh3;

@@ -140,7 +140,8 @@ def cpu_baseline(name: str, target_s: float = 12.0):
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    dt, fl, n = run(16)
+    run(16)  # warms the oracle's threads and caches
+    dt, fl, n = run(128)  # the per-row time of a short pilot sizes the sample
     per_row = max(dt / n, 1e-6)
     n_rows = int(min(w.total_tokens, max(16, target_s / per_row)))
     dt, fl, n = run(n_rows)

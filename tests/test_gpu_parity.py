@@ -110,6 +110,16 @@ def test_one_image_at_an_offset_through_the_raw_abi(head_dim):
             assert err <= TOL[inputs.BF16], err
 
 
+@pytest.mark.parametrize("length,causal", [(1024, False), (1025, False), (3840, False), (3841, False),
+                                           (3841, True), (64, True)])
+def test_one_image_on_both_sides_of_the_item_size_thresholds(length, causal):
+    # A launch over one image chooses its item size in closed form: at 16 heads and a 512-
+    # workgroup grid, up to 1024 tokens take key-split 32-query items, up to 3840 64-query
+    # items, and longer images 256-query items (a masked launch never splits by keys).
+    w = inputs.custom([length], n_heads=16, head_dim=64, dtype=inputs.BF16, seed=17 + length)
+    check_workload(w, full=False, causal=causal)
+
+
 def test_empty_batch_is_a_noop():
     d = torch.device("cuda:0")
     q = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=d)

@@ -824,11 +824,10 @@ __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], cons
                                               f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
                                               const __bf16* Ks, int kb_next);
 
-template <class C, bool FIRST, bool PREFETCH = false>
-__device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
-                                              f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
-                                              int lane, KFrag<C>* knext = nullptr, const __bf16* Ks = nullptr,
-                                              int kb_next = 0) {
+// The offsets part: S becomes t = c2*s - M in place (FIRST sets M), with the rare raise.
+template <class C, bool FIRST>
+__device__ __forceinline__ void offsets_32(f32x4_t (&S)[2][C::QB], f32x4_t (&O)[C::NACC][C::QB],
+                                           float (&negM)[C::QB], float c2, int kinv, int lane) {
   int g = lane >> 4;
   // (opaque in the first step: otherwise the key positions 16kb + 4g + r it compares are
   // hoisted out of the item loop as eight registers held for the whole launch)
@@ -889,11 +888,51 @@ __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf
       }
     }
   }
+}
+
+template <class C, bool FIRST, bool PREFETCH = false>
+__device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
+                                              f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
+                                              int lane, KFrag<C>* knext = nullptr, const __bf16* Ks = nullptr,
+                                              int kb_next = 0) {
+  offsets_32<C, FIRST>(S, O, negM, c2, kinv, lane);
   weights_pv_32<C, PREFETCH>(S, Vs, kb0, O, lane, knext, Ks, kb_next);
 }
 
 // The weights exp2(t) of one 32-key step (t = c2*s - M per element, -inf for no weight),
-// rounded to the element kind, and O^T += V^T.P^T with the row sums alongside.
+// rounded to the element kind.
+template <class C>
+__device__ __forceinline__ void weights_32(const f32x4_t (&S)[2][C::QB], u32x4_t (&W)[C::QB]) {
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      W[qb][j] = cvt_pk<C::E>(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
+                             __builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2 + 1]));
+}
+
+// O^T += V^T.P^T for one 32-key step, with the row sums alongside (an MFMA of the rounded
+// weights against a block of ones), as one matrix burst at raised issue priority.
+template <class C>
+__device__ __forceinline__ void pv_32(const VFrag<C>& V, const u32x4_t (&W)[C::QB], f32x4_t (&O)[C::NACC][C::QB]) {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+      O[db][qb] = mma32<C::E>(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb]);
+  const u32x4_t ones = {kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>};
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+    O[C::NDB][qb] = mma32<C::E>(__builtin_bit_cast(bf16x8_t, ones), __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb]);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The weights of one 32-key step and O^T += V^T.P^T with the row sums alongside.
 template <class C, bool PREFETCH>
 __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
@@ -905,28 +944,8 @@ __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], cons
   load_v<C>(V, Vs, kb0, lane);
   if constexpr (PREFETCH) load_k<C>(*knext, Ks, kb_next, lane);  // the next step's K, same tile
   u32x4_t W[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      W[qb][j] = cvt_pk<C::E>(__builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2]),
-                             __builtin_amdgcn_exp2f(S[j >> 1][qb][(j & 1) * 2 + 1]));
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb)
-      O[db][qb] = mma32<C::E>(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb]);
-  // row sums of the rounded weights, by an MFMA against a block of ones
-  const u32x4_t ones = {kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>};
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb)
-    O[C::NDB][qb] = mma32<C::E>(__builtin_bit_cast(bf16x8_t, ones), __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb]);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
-  __builtin_amdgcn_sched_barrier(0);
+  weights_32<C>(S, W);
+  pv_32<C>(V, W, O);
 }
 
 // One 32-key step [kb0, kb0 + 32) of the LDS tile: operand reads, both products, softmax.
@@ -950,6 +969,31 @@ __device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int 
     __builtin_amdgcn_sched_barrier(0);
   }
   softmax_pv_32<C, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
+}
+
+// One 32-key step whose V^T operands are read together with its K operands, before the
+// score products (for items with one 16-query block per wavefront, whose registers leave
+// room for both): the V^T read latency then hides behind the products and the offsets.
+template <class C, bool FIRST>
+__device__ __forceinline__ void step_32_ev(const __bf16* Ks, const __bf16* Vs, int kb0, int kinv,
+                                           const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                           f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int lane) {
+  f32x4_t S[2][C::QB];
+  KFrag<C> kf;
+  load_k<C>(kf, Ks, kb0, lane);
+  VFrag<C> V;
+  load_v<C>(V, Vs, kb0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  qk_32<C>(S, kf, Q, QT);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  offsets_32<C, FIRST>(S, O, negM, c2, kinv, lane);
+  u32x4_t W[C::QB];
+  weights_32<C>(S, W);
+  pv_32<C>(V, W, O);
 }
 
 // A full step whose K fragments were loaded earlier; PREFETCH also loads the next step's
@@ -1179,7 +1223,7 @@ __device__ __forceinline__ void run_item_split(const Item& item, const __bf16* _
   __syncthreads();                                   // every wave's has
   if (ntiles > 1) issue_tile(1);
   if (kinv < C::KSUB) {  // tile 0's step holds at least one key of the image
-    step_32<C, true>((const __bf16*)stage, (const __bf16*)(stage + C::K_BYTES), kb0, max(kinv, 0), Q, QT, O, negM,
+    step_32_ev<C, true>((const __bf16*)stage, (const __bf16*)(stage + C::K_BYTES), kb0, max(kinv, 0), Q, QT, O, negM,
                      c2, lane);
     started = true;
   }
@@ -1189,9 +1233,9 @@ __device__ __forceinline__ void run_item_split(const Item& item, const __bf16* _
     if (t + 1 < ntiles) issue_tile(t + 1);
     const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
     if (started) {
-      step_32<C, false>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
+      step_32_ev<C, false>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
     } else {
-      step_32<C, true>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
+      step_32_ev<C, true>((const __bf16*)buf, (const __bf16*)(buf + C::K_BYTES), kb0, 0, Q, QT, O, negM, c2, lane);
       started = true;
     }
   }

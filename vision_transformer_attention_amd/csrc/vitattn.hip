@@ -1013,6 +1013,32 @@ __device__ __forceinline__ void step_32k(const KFrag<C>& kf, KFrag<C>& knext, co
   softmax_pv_32<C, false, PREFETCH>(S, Vs, kb0, O, negM, c2, 0, lane, &knext, Ks, kb0 + C::KSUB);
 }
 
+// step_32k with the V^T operands read at the start of the step, as in step_32_ev, for up to
+// kEarlyVMaxQB 16-query blocks per wavefront (with four, the V^T fragments held across the
+// score products no longer fit the registers); the next step's K is read once the scores
+// are consumed.
+constexpr int kEarlyVMaxQB = 2;
+template <class C, bool PREFETCH>
+__device__ __forceinline__ void step_32k_ev(const KFrag<C>& kf, KFrag<C>& knext, const __bf16* Ks, const __bf16* Vs,
+                                            int kb0, const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
+                                            f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int lane) {
+  VFrag<C> V;
+  load_v<C>(V, Vs, kb0, lane);
+  f32x4_t S[2][C::QB];
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  qk_32<C>(S, kf, Q, QT);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  offsets_32<C, false>(S, O, negM, c2, 0, lane);
+  if constexpr (PREFETCH) load_k<C>(knext, Ks, kb0 + C::KSUB, lane);
+  u32x4_t W[C::QB];
+  weights_32<C>(S, W);
+  pv_32<C>(V, W, O);
+}
+
 // Q^T operands: lane (c, g) holds row row0+qb*16+c (rows past qend repeat row qend-1),
 // dims ks*32+8g..+8, and for the 16-deep tail dims NK32*32+4g..+4 (zero past D).  A
 // negative scale is folded into Q by flipping its sign bits.
@@ -1149,8 +1175,13 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
     KFrag<C> k0, k1;
     load_k<C>(k0, Ks, 0, lane);
-    step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
-    step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    if constexpr (C::QB <= kEarlyVMaxQB) {
+      step_32k_ev<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      step_32k_ev<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    } else {
+      step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    }
   }
 
   store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);
@@ -1468,8 +1499,13 @@ __device__ __forceinline__ void run_item_masked(const Item& item, const __bf16* 
     const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
     KFrag<C> k0, k1;
     load_k<C>(k0, Ks, 0, lane);
-    step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
-    step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    if constexpr (C::QB <= kEarlyVMaxQB) {
+      step_32k_ev<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      step_32k_ev<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    } else {
+      step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
+    }
   }
   for (; t < ntiles; ++t) {
     begin_tile(t);

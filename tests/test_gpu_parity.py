@@ -120,6 +120,46 @@ def test_one_image_on_both_sides_of_the_item_size_thresholds(length, causal):
     check_workload(w, full=False, causal=causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_hip_graph_capture_and_replay(causal):
+    # With out= given and the host-side cu_seqlens check off, a call allocates nothing and never
+    # waits on the device, so it can be captured into a HIP graph.  Each replay (with eager
+    # work and synchronisations between) must give the eager result bit for bit, and a replay
+    # after new inputs are copied into the same buffers must give the eager result on them.
+    import vision_transformer_attention_amd as vta
+    w = inputs.custom([300, 129, 1, 64], n_heads=4, head_dim=80, dtype=inputs.BF16, seed=21)
+    q, k, v, cu, scale = inputs.make(w)
+    d = torch.device("cuda:0")
+    qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
+    out = torch.empty_like(qd)
+    vta.fwd(qd, kd, vd, cud, scale, out=out, check_cu=False, causal=causal)  # device set-up, outside the graph
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vta.fwd(qd, kd, vd, cud, scale, out=out, check_cu=False, causal=causal)
+    torch.cuda.synchronize()
+    for i in range(3):
+        say(f"graph replay {i} (causal={causal})")
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+    q2, k2, v2, _, _ = inputs.make(inputs.custom([300, 129, 1, 64], n_heads=4, head_dim=80, dtype=inputs.BF16,
+                                                 seed=22))
+    qd.copy_(q2.to(d))
+    kd.copy_(k2.to(d))
+    vd.copy_(v2.to(d))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    fresh = vta.fwd(q2.to(d), k2.to(d), v2.to(d), cud, scale, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fresh)
+    assert not torch.equal(out, eager)
+
+
 def test_empty_batch_is_a_noop():
     d = torch.device("cuda:0")
     q = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device=d)

@@ -90,11 +90,10 @@ typedef enum {
  * several host threads on different streams.  After a first call on a
  * device (which sets up that device's kernel table), a call enqueues kernel
  * launches (one per 512 sequences) and nothing else, so it may be captured
- * into a HIP graph;
- * each replay reads the buffers' contents at that time.  The library never
- * prints, aborts or computes anything on the CPU: a failure is a status code
- * plus a message in vitattn_last_error().  Results are bitwise reproducible
- * for the same inputs and device.
+ * into a HIP graph; each replay reads the buffers' contents at that time.
+ * The library never prints, aborts or computes anything on the CPU: a
+ * failure is a status code plus a message in vitattn_last_error().  Results
+ * are bitwise reproducible for the same inputs and device.
  */
 int vitattn_fwd(const void* q, const void* k, const void* v, void* o,
                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_heads,

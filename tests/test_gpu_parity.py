@@ -191,24 +191,32 @@ def test_head_independence_bitwise():
     assert torch.equal(got[:, 0], base[:, 0]) and torch.equal(got[:, 2], base[:, 2])
 
 
-@pytest.mark.parametrize("name", ["page-912", "packed-varlen-8", "f32-mixed"])
+@pytest.mark.parametrize("name", ["page-912", "packed-varlen-8", "f32-mixed", "long-16384", "packed-window-256",
+                                  "mid-2000"])
 def test_deterministic_bitwise(name):
     # The launch has a fixed schedule (no atomics, no order-dependent reductions), so any
     # run-to-run difference means a race: an LDS buffer reused too early, or a register
     # overwritten while an in-flight matrix instruction still reads it.  page-912 runs the
     # short-image items split by keys between wavefront pairs, packed-varlen-8 the 256-query
-    # ones.
+    # ones; long-16384 (head_dim 128), the narrow window and a 2000-token image (64-query
+    # items) run the steps that read their V^T operands before the score products.
+    window = 0
     if name == "f32-mixed":
         w = inputs.custom([700, 300, 45], n_heads=4, head_dim=80, dtype=inputs.F32, seed=31)
+    elif name == "packed-window-256":
+        w, window = inputs.WORKLOADS["packed-varlen-8"], 256
+    elif name == "mid-2000":
+        w = inputs.custom([2000], n_heads=16, head_dim=80, dtype=inputs.BF16, seed=32)
     else:
         w = inputs.WORKLOADS[name]
+    say(f"[determinism] {name}")
     q, k, v, cu, scale = inputs.make(w)
     d = torch.device("cuda:0")
     qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
     import vision_transformer_attention_amd as vta
-    first = vta.fwd(qd, kd, vd, cud, scale)
+    first = vta.fwd(qd, kd, vd, cud, scale, window=window)
     for _ in range(4):
-        again = vta.fwd(qd, kd, vd, cud, scale)
+        again = vta.fwd(qd, kd, vd, cud, scale, window=window)
         assert torch.equal(first, again)
     torch.cuda.synchronize()
 

@@ -939,7 +939,9 @@ __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], cons
                                               const __bf16* Ks, int kb_next) {
   // The V^T reads are issued only now, after every score MFMA of the step has been
   // consumed: an LDS read may then reuse those MFMAs' operand registers safely, and its
-  // latency still hides behind the exponentials.
+  // latency still hides behind the exponentials.  (step_32_ev and step_32k_ev read them
+  // before the score products instead; there the V^T registers stay live across those
+  // products, so they are no in-flight MFMA's accumulators either.)
   VFrag<C> V;
   load_v<C>(V, Vs, kb0, lane);
   if constexpr (PREFETCH) load_k<C>(*knext, Ks, kb_next, lane);  // the next step's K, same tile

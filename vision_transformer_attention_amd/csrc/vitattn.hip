@@ -612,24 +612,35 @@ __device__ __forceinline__ float max_4groups(float x) {
 }
 
 
-// Wave-wide DMA loads of one K/V tile.  Load i of wave w is the tile's load number
-// wl = w + i*NW; lane l of it fills chunk slot z = (wl or wl - K_LOADS)*64 + l of the
-// K or V area, i.e. key row z / per and chunk z % per (chunks past head_dim repeat
-// the last real chunk, so every byte copied is finite data of that row).
+// Wave-wide DMA loads of one K/V tile.  The K area takes K_LOADS loads and the V area V_LOADS,
+// each load filling 64 consecutive 16-byte chunk slots (lane l of load slot s fills chunk slot
+// s*64 + l: key row (s*64 + l) / per-row chunks, chunk (s*64 + l) % per-row chunks; chunks past
+// head_dim repeat the last real chunk, so every byte copied is finite data of that row).  Wave
+// w issues K slots w, w + NW, ... and then V slots w, w + NW, ...: KPW + VPW loads for every
+// wave, so the issue has no branch.  A slot number past the last load stands for the wave's
+// previous slot, which is loaded twice (the same bytes to the same place, before the same
+// barrier), instead of a branch that skips it.
 template <class C>
 struct Dma {
-  static constexpr int PER_WAVE = (C::LOADS + C::NW - 1) / C::NW;
+  static constexpr int KPW = (C::K_LOADS + C::NW - 1) / C::NW;  // K loads per wave
+  static constexpr int VPW = (C::V_LOADS + C::NW - 1) / C::NW;  // V loads per wave
+  static constexpr int PER_WAVE = KPW + VPW;
+  static_assert(C::K_LOADS > C::NW && C::V_LOADS > C::NW, "each wave has a previous slot to repeat");
 
-  // Byte offset of lane `lane` of load `wl` relative to the tile's row `lead`; rows of the
-  // tile before `lead` are filled with copies of row `lead`.
-  static __device__ __forceinline__ unsigned lane_offset(int wl, int lane, int lead, unsigned row_bytes) {
-    const bool is_k = wl < C::K_LOADS;
-    const unsigned z = (unsigned)((is_k ? wl : wl - C::K_LOADS) * 64 + lane);
-    // divisions by the two constant row lengths (the choice is uniform across the wave)
-    const int zr = (int)(is_k ? z / C::KCH : z / C::VCH);
-    const int zc = (int)(is_k ? z % C::KCH : z % C::VCH);
-    const int row = max(zr, lead) - lead;
-    const int ch = min(zc, C::CH - 1);
+  // wave w's i-th slot of an area of n loads
+  static __device__ __forceinline__ int slot(int wave, int i, int n) {
+    const int s = wave + i * C::NW;
+    return s < n ? s : s - C::NW;
+  }
+
+  // Byte offset of lane `lane` of slot s (in the K area when IS_K) relative to the tile's row
+  // `lead`; rows of the tile before `lead` are filled with copies of row `lead`.
+  template <bool IS_K>
+  static __device__ __forceinline__ unsigned lane_offset(int s, int lane, int lead, unsigned row_bytes) {
+    constexpr int per = IS_K ? C::KCH : C::VCH;
+    const unsigned z = (unsigned)(s * 64 + lane);
+    const int row = max((int)(z / per), lead) - lead;  // division by a constant
+    const int ch = min((int)(z % per), C::CH - 1);
     return (unsigned)row * row_bytes + (unsigned)ch * 16u;
   }
 
@@ -641,42 +652,69 @@ struct Dma {
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int wl = wave + i * C::NW;
-      off[i] = wl < C::LOADS ? lane_offset(wl, ln, 0, row_bytes) : 0u;
-    }
+    for (int i = 0; i < KPW; ++i) off[i] = lane_offset<true>(slot(wave, i, C::K_LOADS), ln, 0, row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) off[KPW + i] = lane_offset<false>(slot(wave, i, C::V_LOADS), ln, 0, row_bytes);
   }
 
-  // Enqueue the tile whose rows are keys [key0 - lead, key0 - lead + BN): rows before key0
-  // (LEAD, the first tile of a sequence whose length is not a multiple of BN) repeat key0.
-  // The loads go through buffer resources based at key0 of this head and bounded by the last
-  // key row of the sequence (key_end - 1), so a lane reads at most that far (an offset past
-  // it would read zeros, never memory outside the sequence).
-  template <bool LEAD>
-  static __device__ __forceinline__ void issue(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-                                               lds_u8_t* buf, int key0, int key_end, int lead, int head,
-                                               int n_heads, unsigned row_bytes, const unsigned (&off)[PER_WAVE],
-                                               int wave, int lane) {
+  // Where a tile's rows come from (wave-uniform): the byte addresses of its first key row in K
+  // and V (this K/V head) and the bytes from there to the end of the sequence's last key row.
+  // advance() steps to the next tile.
+  struct Src {
+    const unsigned char* kp;
+    const unsigned char* vp;
+    long long extent;
+    __device__ __forceinline__ void advance(unsigned row_bytes) {
+      const unsigned step = (unsigned)C::BN * row_bytes;
+      kp += step;
+      vp += step;
+      extent -= step;
+    }
+  };
+  static __device__ __forceinline__ Src src(const __bf16* __restrict__ k, const __bf16* __restrict__ v, int key0,
+                                            int key_end, int head, int n_heads, unsigned row_bytes) {
     const size_t base = ((size_t)key0 * n_heads + head) * C::D;
-    const unsigned long long extent = (unsigned long long)(key_end - key0 - 1) * row_bytes + C::D * 2;
-    const int n_rec = (int)(extent < 0x7fffffffull ? extent : 0x7fffffffull);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, n_rec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, n_rec, 0x00020000);
+    return Src{reinterpret_cast<const unsigned char*>(k + base), reinterpret_cast<const unsigned char*>(v + base),
+               (long long)(key_end - key0 - 1) * row_bytes + C::D * 2};
+  }
+
+  // Enqueue the tile whose rows are keys [key0 - lead, key0 - lead + BN) of `sr` (based at
+  // key0): rows before key0 (LEAD, the first tile of a sequence whose length is not a
+  // multiple of BN) repeat key0.  The loads go through buffer resources based at key0 and
+  // bounded by the last key row of the sequence, so a lane reads at most that far (an offset
+  // past it would read zeros, never memory outside the sequence).
+  template <bool LEAD>
+  static __device__ __forceinline__ void issue(const Src& sr, lds_u8_t* buf, int lead, unsigned row_bytes,
+                                               const unsigned (&off)[PER_WAVE], int wave, int lane) {
+    const int n_rec = (int)(sr.extent < 0x7fffffffll ? sr.extent : 0x7fffffffll);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)sr.kp, (short)0, n_rec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)sr.vp, (short)0, n_rec, 0x00020000);
     // The first tile's offsets are recomputed here each time: an opaque copy of the lane
     // index keeps the compiler from hoisting their per-lane parts out of the item loop, where
     // they would take 12 registers for the whole launch (and be spilled).
     int ln = lane;
     if constexpr (LEAD) asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int wl = wave + i * C::NW;
-      if (wl < C::LOADS) {
-        const bool is_k = wl < C::K_LOADS;
-        const unsigned o = LEAD ? lane_offset(wl, ln, lead, row_bytes) : off[i];
-        lds_u8_t* dst = buf + (is_k ? wl * 1024 : C::K_BYTES + (wl - C::K_LOADS) * 1024);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, (lds_void_t*)dst, 16, o, 0, 0, 0);
-      }
+    for (int i = 0; i < KPW; ++i) {
+      const int s = slot(wave, i, C::K_LOADS);
+      const unsigned o = LEAD ? lane_offset<true>(s, ln, lead, row_bytes) : off[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + s * 1024), 16, o, 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const int s = slot(wave, i, C::V_LOADS);
+      const unsigned o = LEAD ? lane_offset<false>(s, ln, lead, row_bytes) : off[KPW + i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + C::K_BYTES + s * 1024), 16, o, 0, 0, 0);
+    }
+  }
+
+  // The same for a tile given by its first key: the tile [key0 - lead, key0 - lead + BN).
+  template <bool LEAD>
+  static __device__ __forceinline__ void issue(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                                               lds_u8_t* buf, int key0, int key_end, int lead, int head,
+                                               int n_heads, unsigned row_bytes, const unsigned (&off)[PER_WAVE],
+                                               int wave, int lane) {
+    issue<LEAD>(src(k, v, key0, key_end, head, n_heads, row_bytes), buf, lead, row_bytes, off, wave, lane);
   }
 };
 
@@ -1120,6 +1158,12 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     Dma<C>::template issue<true>(k, v, stage, item.a, item.b, pad, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
   else
     Dma<C>::template issue<false>(k, v, stage, item.a, item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+  // tile t >= 1 starts at key kstart + t*BN; sr follows the next tile to issue
+  typename Dma<C>::Src sr = Dma<C>::src(k, v, kstart + C::BN, item.b, kv_head, n_kv_heads, row_bytes);
+  auto issue_next = [&](int t) {  // tile t (>= 1) into buffer t & 1
+    Dma<C>::template issue<false>(sr, stage + (t & 1) * C::STAGE_BYTES, 0, row_bytes, dma_off, wave, lane);
+    sr.advance(row_bytes);
+  };
 
   if (row0 >= qend) {
     // No row of this wavefront lies in the sequence (the last, partial item of an image): it
@@ -1128,9 +1172,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     for (int t = 0; t < ntiles; ++t) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (t + 1 < ntiles)
-        Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN,
-                                      item.b, 0, kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+      if (t + 1 < ntiles) issue_next(t + 1);
     }
     return;
   }
@@ -1149,9 +1191,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   // tile 0: the first step with a key in the sequence sets the exponent offsets
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile 0 has landed
   __syncthreads();                                   // every wave's has
-  if (ntiles > 1)
-    Dma<C>::template issue<false>(k, v, stage + C::STAGE_BYTES, kstart + C::BN, item.b, 0, kv_head, n_kv_heads, row_bytes,
-                                  dma_off, wave, lane);
+  if (ntiles > 1) issue_next(1);
   const int s0 = pad / C::KSUB;
   {
     const __bf16* Ks = (const __bf16*)(stage);
@@ -1169,9 +1209,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   for (int t = 1; t < ntiles; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
     __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
-    if (t + 1 < ntiles)
-      Dma<C>::template issue<false>(k, v, stage + ((t + 1) & 1) * C::STAGE_BYTES, kstart + (t + 1) * C::BN, item.b, 0,
-                                    kv_head, n_kv_heads, row_bytes, dma_off, wave, lane);
+    if (t + 1 < ntiles) issue_next(t + 1);
     const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
     const __bf16* Ks = (const __bf16*)(buf);
     const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
@@ -1215,6 +1253,7 @@ __device__ __forceinline__ void run_item_split(const Item& item, const __bf16* _
   unsigned dma_off[Dma<C>::PER_WAVE];  // computed per item (see Dma::init), not held across items
   Dma<C>::init(dma_off, wave, lane, row_bytes);
   static_assert(C::NSUB == 2 && C::NW % 2 == 0, "two 32-key steps per tile, wavefronts in pairs");
+  static_assert(C::QB == 1, "the merge below hands over one 16-query block per wavefront");
   constexpr int BM = C::NW / 2 * C::NQ;  // queries per item
   constexpr int NV = C::NACC * 4 + 1;    // floats per lane handed over: output, row sum, offset
   static_assert(C::NW / 2 * NV * 64 * 4 <= 2 * C::STAGE_BYTES, "merge area fits the stage buffers");
@@ -1225,9 +1264,11 @@ __device__ __forceinline__ void run_item_split(const Item& item, const __bf16* _
   const int ntiles = ceil_div(item.b - item.a, C::BN);
   const int pad = ntiles * C::BN - (item.b - item.a);  // 0 <= pad < BN
   const int kstart = item.a - pad;
+  // tiles t >= 1 are issued in order; sr follows the next one
+  typename Dma<C>::Src sr = Dma<C>::src(k, v, kstart + C::BN, item.b, kv_head, n_kv_heads, row_bytes);
   auto issue_tile = [&](int t) {  // tile t >= 1 into buffer t & 1
-    Dma<C>::template issue<false>(k, v, stage + (t & 1) * C::STAGE_BYTES, kstart + t * C::BN, item.b, 0, kv_head,
-                                  n_kv_heads, row_bytes, dma_off, wave, lane);
+    Dma<C>::template issue<false>(sr, stage + (t & 1) * C::STAGE_BYTES, 0, row_bytes, dma_off, wave, lane);
+    sr.advance(row_bytes);
   };
 
   __syncthreads();  // the previous item is done with the stage buffers (and the merge area)

@@ -1,18 +1,31 @@
 """Benchmark: attention TFLOP/s of the HIP path on one MI355X.
 
-One step is one ``vitattn_fwd`` call (the whole hot path: work planning, K/V
-staging, both MFMA products, online softmax and the epilogue) over one batch of
-seeded synthetic input.  The headline workload is the packed variable-length
-batch (8 images, 17,408 tokens, 16 heads of 80, bf16); the 912-patch page
-(16 heads of 80, bf16), also named by the metric, is timed beside it.  FLOPs are
-4 * sum_s L_s^2 * D * H with the true head_dim.  Inputs are resident in HBM before
-the timed region starts.
+One step is one attention call (the whole hot path: work planning, K/V staging, both
+MFMA products, online softmax and the epilogue) over one batch of seeded synthetic
+input.  The headline workload is the packed variable-length batch (8 images, 17,408
+tokens, 16 heads of 80, bf16); every other workload of the metric's family is timed
+beside it in ``configs``: the tiny float32 case, the 196-patch ViT image, the 912-patch
+page and the 16,384-token sequence.  The three small ones are also replayed from a HIP
+graph of 50 captured calls, since their eager launches are bound by the host's enqueue
+time (``graph_replay_ms_per_step``).  FLOPs are 4 * sum_s L_s^2 * D * H with the true head_dim.
+Inputs are resident in HBM before any timed region starts.
+
+Timing per workload: one call for the library's one-time device set-up, then ``--warmup``
+launches timed as a block (the cold figure, reported as ``cold_ms_per_step``), then untimed
+launches until ``--settle-ms`` of device time has passed
+(the GPU needs about 30 ms of work to reach its steady clock), then exactly ``--steps``
+launches between two HIP events on the launch stream.
+
+The CPU leg times the float64 oracle on the host's cores (all of them, then one) on a
+bounded sample of the headline workload, and compares each workload's GPU output with
+the oracle on a bounded set of rows (``max_abs_err`` in ``configs``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,15 +34,25 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "attention TFLOP/s (4*S^2*D*H) at S=912,D=80 and packed varlen; % bf16 MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (and f16) MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "packed-varlen-8"
-SECONDARY = "page-912"
+FAMILY = ("tiny-64", "vit-196", "page-912", "packed-varlen-8", "long-16384")
 PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "vision_transformer_attention_amd", "csrc", "vitattn.hip")
+# rows of each workload the oracle recomputes for max_abs_err (None: every row)
+ERR_ROWS = {"tiny-64": None, "vit-196": None, "page-912": None, "packed-varlen-8": 2048, "long-16384": 192}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 1e-2}
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+def peak_of(dtype: str) -> float:
+    return FP32_PEAK_TFLOPS if dtype == "f32" else BF16_PEAK_TFLOPS  # dense f16 MFMA = dense bf16
 
 
 def visible_pairs(lengths, causal: bool, window: int) -> int:
@@ -48,8 +71,66 @@ def visible_pairs(lengths, causal: bool, window: int) -> int:
     return total
 
 
-def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False, causal: bool = False,
-                  window: int = 0):
+def timed_launches(call, steps: int, warmup: int, settle_ms: float):
+    """(cold ms per launch over the warm-up, settle ms actually run, ms per launch over `steps`)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    call()  # the library's one-time device set-up happens outside every timed region
+    torch.cuda.synchronize()
+    cold = None
+    if warmup > 0:
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(warmup):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold = a.elapsed_time(b) / warmup
+    settled = 0.0
+    while settled < settle_ms:  # untimed: until the device has worked settle_ms
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(20):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        settled += a.elapsed_time(b)
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return cold, settled, start.elapsed_time(end) / steps
+
+
+def graph_replay_ms(call, per_graph: int = 50, replays: int = 20) -> float:
+    """ms per call when `per_graph` calls are captured into one HIP graph and replayed."""
+    import torch
+    call()  # device set-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * per_graph)
+
+
+def attention_case(name: str, out_f32: bool = False, causal: bool = False, window: int = 0):
+    """Device inputs for a workload and a zero-argument call of the binding on them."""
     import torch
 
     import vision_transformer_attention_amd as vta
@@ -58,32 +139,27 @@ def time_workload(name: str, steps: int, warmup: int, out_f32: bool = False, cau
     w = inputs.WORKLOADS[name]
     q, k, v, cu, scale = inputs.make(w)
     dev = torch.device("cuda:0")
-    q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+    qd, kd, vd, cud = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
     out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False, causal=causal, window=window)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
-        vta.fwd(q, k, v, cu, scale, out=out, check_cu=False, causal=causal, window=window)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = start.elapsed_time(end) / steps  # events on the launch stream
-    cfg = vta.binding.kernel_config(w.head_dim, q.dtype)
-    return w, kernel_ms, wall * 1e3 / steps, cfg
+
+    def call():
+        vta.fwd(qd, kd, vd, cud, scale, out=out, causal=causal, window=window)
+
+    return w, (q, k, v, cu, scale), out, call
 
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+def time_workload(name: str, steps: int, warmup: int, settle_ms: float, graph: bool = False, **kw):
+    w, host, out, call = attention_case(name, **kw)
+    cold, settled, ms = timed_launches(call, steps, warmup, settle_ms)
+    rec = {"workload": name, "ms_per_step": ms, "cold_ms_per_step": cold, "settle_ms": settled, "steps": steps}
+    if graph:
+        rec["graph_replay_ms_per_step"] = graph_replay_ms(call)
+    return w, host, out, rec
 
 
-def time_prologue(name: str, steps: int, warmup: int):
+def time_prologue(name: str, steps: int, warmup: int, settle_ms: float):
     """The qkv prologue (split + per-head RMS norm + rope) on the workload's token count and
-    heads; returns (seconds per launch, algorithmic bytes per launch)."""
+    heads; returns (workload, ms per launch, algorithmic bytes per launch)."""
     import torch
 
     import vision_transformer_attention_amd as vta
@@ -96,25 +172,38 @@ def time_prologue(name: str, steps: int, warmup: int):
     args = (mv(d["qkv"]), d["n_heads"], d["n_kv_heads"], mv(d["cos"]), mv(d["sin"]), mv(d["q_weight"]),
             mv(d["k_weight"]))
     out = vta.qkv_prologue(*args)
-    for _ in range(warmup):
-        vta.qkv_prologue(*args, out=out)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream(dev)
-    start.record(stream)
-    for _ in range(steps):
-        vta.qkv_prologue(*args, out=out)
-    end.record(stream)
-    torch.cuda.synchronize()
-    sec = start.elapsed_time(end) / steps * 1e-3
+    _, _, ms = timed_launches(lambda: vta.qkv_prologue(*args, out=out), steps, warmup, settle_ms)
     es = d["qkv"].element_size()
     t = d["qkv"].shape[0]
     nbytes = 2 * d["qkv"].numel() * es + 2 * t * w.head_dim * 4 + 2 * w.head_dim * 4
-    return w, sec, nbytes
+    return w, ms, nbytes
 
 
-def cpu_baseline(name: str, target_s: float = 12.0):
-    """The float64 oracle timed on the host's cores on a bounded sample of query rows."""
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_counters(name: str):
+    """The committed rocprofv3 counter summary of this workload's attention kernel, when it was
+    taken on the current kernel source (else None): MFMA-busy fraction and HBM bytes per launch."""
+    path = os.path.join(PROFILES, f"attn_fwd_{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_sha():
+        return None
+    return rec
+
+
+def cpu_leg(name: str, gpu_outputs: dict, target_s: float = 10.0, one_core_s: float = 8.0):
+    """The float64 oracle: timed on the host cores (all, then one) on a bounded sample of the
+    headline workload's query rows, and compared with each workload's GPU output on a bounded
+    set of rows.  Returns (cpu_baseline record, {workload: error record})."""
     import numpy as np
 
     import oracle
@@ -122,8 +211,7 @@ def cpu_baseline(name: str, target_s: float = 12.0):
 
     w = inputs.WORKLOADS[name]
     q, k, v, cu, scale = inputs.make(w)
-    cu_np = cu.numpy()
-    lens = np.diff(cu_np)
+    lens = np.diff(cu.numpy())
     seq_of = np.repeat(np.arange(len(lens)), lens)
     rng = np.random.default_rng(123)
 
@@ -134,54 +222,65 @@ def cpu_baseline(name: str, target_s: float = 12.0):
         oracle.attention_rows(q, k, v, cu, scale, rows)
         return time.perf_counter() - t0, flops, n_rows
 
+    def timed(budget_s):
+        run(16)  # warms the oracle's threads and caches
+        dt, _, n = run(128)  # the per-row time of a short pilot sizes the sample
+        n_rows = int(min(w.total_tokens, max(16, budget_s / max(dt / n, 1e-6))))
+        return run(n_rows)
+
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    run(16)  # warms the oracle's threads and caches
-    dt, fl, n = run(128)  # the per-row time of a short pilot sizes the sample
-    per_row = max(dt / n, 1e-6)
-    n_rows = int(min(w.total_tokens, max(16, target_s / per_row)))
-    dt, fl, n = run(n_rows)
-    return {
+    cores = oracle.threads()
+    dt, fl, n = timed(target_s)
+    oracle.set_threads(1)
+    dt1, fl1, n1 = timed(one_core_s)
+    oracle.set_threads(cores)
+    base = {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": oracle.threads(),
+        "cores": cores,
         "cpu_model": model,
         "kind": "oracle",
         "sample": f"{n} of {w.total_tokens} query rows of {name} (all {w.n_heads} heads, every key of each row's "
-                  f"image), float64, {dt:.1f} s",
+                  f"image), float64, {dt:.1f} s on {cores} threads",
+        "one_core": {"value": fl1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                     "sample": f"{n1} query rows of {name}, {dt1:.1f} s on 1 thread"},
     }
-
-
-def load_traffic(name: str):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
-    when there is none for this workload or the kernel source changed since it was taken."""
-    import hashlib
-
-    path = os.path.join(PROFILES, f"attn_fwd_bf16_d80_{name}_hbm_traffic.json")
-    src = os.path.join(ROOT, "vision_transformer_attention_amd", "csrc", "vitattn.hip")
-    if not os.path.exists(path):
-        return None
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("source_sha256") != sha:
-            return None
-        return rec.get("bytes_per_launch")
-    except Exception:
-        return None
+    errs = {}
+    for wname, (host, out) in gpu_outputs.items():
+        wq, wk, wv, wcu, wscale = host
+        ww = inputs.WORKLOADS[wname]
+        g = out.float().cpu().numpy().astype(np.float64)
+        n_rows = ERR_ROWS.get(wname)
+        if n_rows is None or n_rows >= ww.total_tokens:
+            ref = oracle.attention(wq, wk, wv, wcu, wscale)
+            rows = None
+        else:
+            rows = np.sort(np.random.default_rng(7).choice(ww.total_tokens, size=n_rows, replace=False))
+            ref = oracle.attention_rows(wq, wk, wv, wcu, wscale, rows.astype(np.int64))
+            g = g[rows]
+        diff = np.abs(g - ref)
+        at = np.unravel_index(int(np.argmax(diff)), diff.shape)
+        row = int(rows[at[0]]) if rows is not None else int(at[0])
+        errs[wname] = {"max_abs_err": float(diff[at]), "at": [row, int(at[1]), int(at[2])],
+                       "mean_abs_err": float(diff.mean()), "tol": TOL[ww.dtype],
+                       "rows_compared": int(g.shape[0]), "rows": int(ww.total_tokens)}
+        log(f"[bench] {wname}: max-abs err {errs[wname]['max_abs_err']:.3e} at {errs[wname]['at']} "
+            f"over {g.shape[0]} rows (tol {TOL[ww.dtype]})")
+    return base, errs
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed device time run after the warm-up, before the timed launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-secondary", action="store_true", help="time only --workload (for profiling runs)")
@@ -195,8 +294,8 @@ def main():
                     help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path here is a "
-              f"single-GPU build, see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this attention path is a single-GPU "
+              f"build; DESIGN.md describes how it would shard.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -204,13 +303,13 @@ def main():
         sys.exit(1)
 
     if args.prologue:
-        w, sec, nbytes = time_prologue(args.workload, args.steps, args.warmup)
-        gbs = nbytes / sec / 1e9
-        log(f"[bench] prologue {args.workload}: {sec * 1e6:.1f} us/launch, {gbs:.0f} GB/s")
+        w, ms, nbytes = time_prologue(args.workload, args.steps, args.warmup, args.settle_ms)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"[bench] prologue {args.workload}: {ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s")
         print(json.dumps({
             "metric": "qkv prologue GB/s (packed qkv read once, Q/K/V written once, rope tables read once)",
             "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": w.dtype, "data": "synthetic (seeded N(0,1) projection output, 2-D rope tables)",
             "config": {"workload": w.name, "tokens": w.total_tokens, "heads": w.n_heads, "kv_heads": w.kv_heads,
                        "head_dim": w.head_dim, "bytes_per_step": nbytes, "rope": True, "norm": True},
@@ -218,14 +317,19 @@ def main():
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         }), flush=True)
         return
-    log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
+
     masked = args.causal or args.window > 0
-    w, kernel_ms, wall_ms, cfg = time_workload(args.workload, args.steps, args.warmup, args.out_dtype == "f32",
-                                               args.causal, args.window)
+    out_f32 = args.out_dtype == "f32"
+    log(f"[bench] {args.workload}: warmup {args.warmup}, settle {args.settle_ms:.0f} ms, steps {args.steps}")
+    w, host, out, rec = time_workload(args.workload, args.steps, args.warmup, args.settle_ms, out_f32=out_f32,
+                                      causal=args.causal, window=args.window)
+    kernel_ms = rec["ms_per_step"]
     # algorithmic FLOPs: 4*D*H per (query, key) pair the mask keeps
     flops = (4.0 * w.head_dim * w.n_heads * visible_pairs(w.lengths, args.causal, args.window)) if masked else w.flops
     tflops = flops / (kernel_ms * 1e-3) / 1e12
-    log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    peak = peak_of(w.dtype)
+    log(f"[bench] {args.workload}: {kernel_ms * 1e3:.1f} us/launch ({tflops:.1f} TFLOP/s, {tflops / peak:.1%} of "
+        f"peak); cold {rec['cold_ms_per_step'] * 1e3 if rec['cold_ms_per_step'] else 0:.1f} us/launch")
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -235,51 +339,79 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written once")
         del src, dst
-    sec = None
-    if args.workload != SECONDARY and not args.no_secondary and not masked:
-        log(f"[bench] timing {SECONDARY}")
-        w2, k2, wall2, cfg2 = time_workload(SECONDARY, max(args.steps, 200), args.warmup)
-        sec = {"workload": SECONDARY, "value": w2.flops / (k2 * 1e-3) / 1e12, "unit": "TFLOP/s",
-               "ms_per_step": k2, "frac_of_bf16_peak": w2.flops / (k2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-        log(f"[bench] {SECONDARY}: {k2 * 1e3:.1f} us/launch, {sec['value']:.1f} TFLOP/s")
+
+    outputs = {}  # workload -> (host inputs, GPU output) for the oracle comparison
+    configs = {}
+    family = not (args.no_secondary or masked or out_f32) and args.workload in FAMILY
+    if family:
+        outputs[args.workload] = (host, out)
+        for name in FAMILY:
+            if name == args.workload:
+                r = dict(rec)
+                ww = w
+            else:
+                ww, h2, o2, r = time_workload(name, args.steps if name != "long-16384" else max(10, args.steps // 10),
+                                              args.warmup, min(args.settle_ms, 50.0),
+                                              graph=name in ("tiny-64", "vit-196", "page-912"))
+                outputs[name] = (h2, o2)
+            pk = peak_of(ww.dtype)
+            r.update({"value": ww.flops / (r["ms_per_step"] * 1e-3) / 1e12, "unit": "TFLOP/s", "dtype": ww.dtype,
+                      "lengths": list(ww.lengths) if len(ww.lengths) <= 16 else len(ww.lengths),
+                      "heads": ww.n_heads, "head_dim": ww.head_dim, "flops_per_step": ww.flops, "peak": pk})
+            r["frac_of_peak"] = r["value"] / pk
+            if "graph_replay_ms_per_step" in r:
+                r["graph_replay_value"] = ww.flops / (r["graph_replay_ms_per_step"] * 1e-3) / 1e12
+            configs[name] = r
+            log(f"[bench] {name}: {r['ms_per_step'] * 1e3:.2f} us/launch, {r['value']:.1f} TFLOP/s "
+                f"({r['frac_of_peak']:.1%} of {pk})"
+                + (f"; graph replay {r['graph_replay_ms_per_step'] * 1e3:.2f} us" if "graph_replay_ms_per_step" in r
+                   else ""))
+
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the float64 oracle on the host cores (bounded sample)")
-        cpu = cpu_baseline(args.workload)
-        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
-    dtype = w.dtype  # the element type the products are computed in: "bf16", "f16" or "f32"
-    peak = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS  # dense f16 MFMA = dense bf16
-    rec = {
-        "metric": "attention TFLOP/s (4*S^2*D*H summed over sequences)",
+        log("[bench] the float64 oracle on the host cores (bounded samples)")
+        cpu, errs = cpu_leg(args.workload if args.workload in FAMILY else HEADLINE, outputs)
+        for name, e in errs.items():
+            configs.setdefault(name, {}).update(e)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads, "
+            f"{cpu['one_core']['value'] * 1e3:.3f} on 1")
+
+    counters = committed_counters(w.name) if not (masked or out_f32) else None
+    traffic = counters.get("hbm_bytes_per_launch") if counters else None
+    result = {
+        "metric": METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": kernel_ms,
-        "wall_ms_per_step": wall_ms,
+        "cold_ms_per_step": rec["cold_ms_per_step"],
+        "settle_ms": rec["settle_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {
             "workload": w.name, "lengths": list(w.lengths), "tokens": w.total_tokens, "heads": w.n_heads,
-            "head_dim": w.head_dim, "kv_heads": w.kv_heads, "out_dtype": "f32" if args.out_dtype == "f32" else w.dtype,
-            "causal": bool(args.causal), "window": args.window,
+            "head_dim": w.head_dim, "kv_heads": w.kv_heads, "out_dtype": "f32" if out_f32 else w.dtype,
+            "causal": bool(args.causal), "window": args.window, "flops_per_step": flops,
             "caches": "warm: inputs resident in HBM, launches back to back on one stream",
-            "flops_per_step": flops, "block_m": None if masked else cfg["block_m"],
-            "block_n": cfg["block_n"], "waves_per_workgroup": cfg["waves"], "grid": cfg["grid"],
         },
         "roofline": {
-            "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": tflops / peak,
-            "traffic": load_traffic(w.name) if args.out_dtype == "same" and not masked else None,
+            "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+            "traffic": traffic,
+            "traffic_source": (f"profiles/attn_fwd_{w.name}_counters.json: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                               f"of this kernel source, scaled by a plain copy" if traffic else None),
         },
-        "secondary": sec,
+        "counters": ({"source": f"profiles/attn_fwd_{w.name}_counters.json (rocprofv3, this kernel source)",
+                      "mfma_busy": counters.get("mfma_busy"), "hbm_gbs": counters.get("hbm_gbs"),
+                      "trace_mean_us": counters.get("trace_mean_us")} if counters else None),
+        "configs": configs or None,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -93,6 +93,8 @@ def _bind(lib):
     lib.vitattn_ref_row_probs_f64.restype = ctypes.c_int64
     lib.vitattn_ref_threads.argtypes = []
     lib.vitattn_ref_threads.restype = ctypes.c_int
+    lib.vitattn_ref_set_threads.argtypes = [ctypes.c_int]
+    lib.vitattn_ref_set_threads.restype = None
     return lib
 
 
@@ -262,3 +264,8 @@ def qkv_prologue(qkv, n_heads: int, n_kv_heads: int, cos=None, sin=None, q_weigh
 def threads() -> int:
     """OpenMP threads the oracle's parallel regions use."""
     return int(load().vitattn_ref_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads from now on (the results do not depend on it)."""
+    load().vitattn_ref_set_threads(int(n))

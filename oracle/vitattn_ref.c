@@ -124,6 +124,16 @@ int vitattn_ref_threads(void) {
 #endif
 }
 
+/* Sets the number of threads later OpenMP regions here use (n >= 1; no effect without OpenMP).
+   Only the speed of the oracle changes: every output is computed by one thread in a fixed order. */
+void vitattn_ref_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Full output o[T, H, D] (float64) for q [T, H, D] and k, v [T, Hkv, D]
  * (float32 values), Hkv a divisor of H, under the mask rules (causal 0 or 1,
  * window >= 0).  Returns 0, or -1 on a bad argument or an allocation failure. */

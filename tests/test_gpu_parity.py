@@ -23,15 +23,28 @@ def test_workload_full(name):
     check_workload(inputs.WORKLOADS[name], full=True)
 
 
-def test_packed_varlen_sampled_rows():
-    check_workload(inputs.WORKLOADS["packed-varlen-8"], full=False)
+def test_packed_varlen_every_row():
+    # the full packed batch, every one of its 17,408 rows (the launch the benchmark times)
+    check_workload(inputs.WORKLOADS["packed-varlen-8"], full=True)
 
 
-def test_long_sequence_sampled_rows_and_convex_hull():
+def long_rows() -> np.ndarray:
+    """1,024 rows of the 16,384-token sequence: at head_dim 128 a work item is 128 query rows,
+    4 wavefronts of two 16-row blocks; every item contributes one row of every block of every
+    wavefront, at a lane position that varies from item to item, plus the sequence's ends."""
+    rows = []
+    for item in range(128):
+        for wave in range(4):
+            for qb in range(2):
+                rows.append(item * 128 + wave * 32 + qb * 16 + (item * 7 + wave * 3 + qb * 5) % 16)
+    rows = sorted(set(rows) | {0, 1, 16382, 16383})
+    return np.array(rows, np.int64)
+
+
+def test_long_sequence_rows_of_every_item_and_convex_hull():
     w = inputs.WORKLOADS["long-16384"]
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, 8191, 8192, 16382, 16383],
-                                     rng.integers(0, 16384, 23)])).astype(np.int64)
+    rows = long_rows()
+    assert len(rows) >= 1024
     o, _ = check_workload(w, full=False, rows=rows)
     _, _, v, _, _ = inputs.make(w)
     vf, of = v.float(), o.float()
@@ -58,6 +71,15 @@ def test_rising_and_jumping_scores(dtype, head_dim):
     ramp = 40.0 if dtype == inputs.F32 else 300.0
     w = inputs.custom([1000, 777, 64, 33, 5], n_heads=2, head_dim=head_dim, dtype=dtype, seed=23, key_ramp=ramp,
                       spikes=2)
+    check_workload(w, full=True)
+
+
+@pytest.mark.parametrize("head_dim", [64, 80])
+def test_rising_and_jumping_scores_in_large_items(head_dim):
+    # The same drift and spikes at 16 heads over long images, so that the launch runs its
+    # 256-query items (the path of the packed batch) and raises their offsets many times.
+    w = inputs.custom([3000, 2500, 1200, 777, 33, 5], n_heads=16, head_dim=head_dim, dtype=inputs.BF16, seed=29,
+                      key_ramp=300.0, spikes=2)
     check_workload(w, full=True)
 
 
@@ -108,6 +130,31 @@ def test_one_image_at_an_offset_through_the_raw_abi(head_dim):
                                    scale)
             err = float(np.max(np.abs(o[lo:hi].float().numpy().astype(np.float64) - ref)))
             assert err <= TOL[inputs.BF16], err
+
+
+def test_default_call_does_not_synchronise():
+    # With cu_seqlens on the device the default call only enqueues work: under torch's
+    # sync debug mode "error" any host synchronisation (such as reading cu_seqlens back
+    # for a check) raises.
+    import vision_transformer_attention_amd as vta
+    w = inputs.custom([300, 129, 1, 64], n_heads=4, head_dim=80, dtype=inputs.BF16, seed=31)
+    q, k, v, cu, scale = inputs.make(w)
+    d = torch.device("cuda:0")
+    qd, kd, vd, cud = q.to(d), k.to(d), v.to(d), cu.to(d)
+    vta.fwd(qd, kd, vd, cud, scale)  # device set-up (kernel table) outside the checked region
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        o = vta.fwd(qd, kd, vd, cud, scale)
+        oc = vta.fwd(qd, kd, vd, cud, scale, causal=True, out_dtype=torch.float32)
+    finally:
+        torch.cuda.set_sync_debug_mode("default")
+    torch.cuda.synchronize()
+    for got, causal in ((o, False), (oc, True)):
+        ref = oracle.attention(q, k, v, cu, scale, causal=causal)
+        err = float(np.max(np.abs(got.float().cpu().numpy().astype(np.float64) - ref)))
+        say(f"[parity] async default call causal={causal}: max-abs err {err:.3e}")
+        assert err <= TOL[inputs.BF16], err
 
 
 @pytest.mark.parametrize("length,causal", [(1024, False), (1025, False), (3840, False), (3841, False),

@@ -146,21 +146,27 @@ def fwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, 
                                        ctypes.c_float(scale), causal, window, dtype_code, stream))
 
 
-def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool = True, out_dtype=None,
+def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: bool | None = None, out_dtype=None,
         causal: bool = False, window: int = 0):
     """Attention over packed sequences; returns ``o`` like ``q``.
 
-    q: contiguous CUDA (HIP) tensor ``[T, H, D]`` of bfloat16 or float32, D in
+    q: contiguous GPU tensor ``[T, H, D]`` of bfloat16, float16 or float32, D in
     {64, 72, 80, 128}; k, v: the same dtype, ``[T, Hkv, D]`` with Hkv dividing H
     (Hkv < H is grouped-query attention: query head h uses K/V head
-    ``h // (H // Hkv)``).  cu_seqlens: int32 ``[n_seqs + 1]`` prefix array on the
-    same device (a CPU copy is checked on the host when ``check_cu``).  scale
-    defaults to ``1/sqrt(D)``; any finite value (1.0 included) is passed through
-    unchanged.  The output has q's dtype, or ``out_dtype`` (or ``out``'s dtype):
-    bfloat16 and float16 inputs may be written as float32.  By default every
-    query sees every key of its sequence (bidirectional); ``causal`` keeps the
-    keys at or before the query and ``window`` > 0 the keys less than
-    ``window`` positions from it (both within the sequence).
+    ``h // (H // Hkv)``).  The inputs must be finite: the kernels are built on that
+    precondition, and a NaN or infinity in q, k or v (or a score that overflows
+    float32) gives undefined results rather than NaN rows.  cu_seqlens: int32
+    ``[n_seqs + 1]`` prefix array (0, non-decreasing, ending at T).  On q's device it
+    is passed to the kernel as it is, and the call neither waits for the device nor
+    allocates anything beyond ``out`` (so it can be captured into a HIP graph when
+    ``out`` is given); ``check_cu=True`` checks it on the host first, which waits for
+    the device.  A CPU tensor is checked on the host (unless ``check_cu=False``) and
+    copied to the device.  scale defaults to ``1/sqrt(D)``; any finite value (1.0
+    included) is passed through unchanged.  The output has q's dtype, or
+    ``out_dtype`` (or ``out``'s dtype): bfloat16 and float16 inputs may be written as
+    float32.  By default every query sees every key of its sequence (bidirectional);
+    ``causal`` keeps the keys at or before the query and ``window`` > 0 the keys less
+    than ``window`` positions from it (both within the sequence).
     """
     import torch
     lib = load_library()
@@ -190,9 +196,10 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
         raise ValueError(f"head_dim {head_dim} not in {HEAD_DIMS}")
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise TypeError("cu_seqlens must be a 1-D int32 torch tensor")
-    if check_cu:
+    on_device = cu_seqlens.device == q.device
+    if check_cu or (check_cu is None and not on_device):
         check_cu_seqlens(cu_seqlens.cpu().numpy(), t_tokens)
-    cu_dev = cu_seqlens if cu_seqlens.device == q.device else cu_seqlens.to(q.device)
+    cu_dev = cu_seqlens if on_device else cu_seqlens.to(q.device)
     if not cu_dev.is_contiguous():
         cu_dev = cu_dev.contiguous()
     if scale is None:

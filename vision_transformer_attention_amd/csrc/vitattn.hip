@@ -857,7 +857,7 @@ __device__ __forceinline__ void qk_32(f32x4_t (&S)[2][C::QB], const KFrag<C>& K,
 //
 // Only the FIRST step of an item can hold keys outside the sequence: its first `kinv`
 // keys, which take no part in the max and get weight exactly 0 (also when c2 is 0).
-template <class C, bool PREFETCH>
+template <class C, bool PREFETCH, bool ZERO = false>
 __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
                                               const __bf16* Ks, int kb_next);
@@ -928,13 +928,13 @@ __device__ __forceinline__ void offsets_32(f32x4_t (&S)[2][C::QB], f32x4_t (&O)[
   }
 }
 
-template <class C, bool FIRST, bool PREFETCH = false>
+template <class C, bool FIRST, bool PREFETCH = false, bool ZERO = false>
 __device__ __forceinline__ void softmax_pv_32(f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], float (&negM)[C::QB], float c2, int kinv,
                                               int lane, KFrag<C>* knext = nullptr, const __bf16* Ks = nullptr,
                                               int kb_next = 0) {
   offsets_32<C, FIRST>(S, O, negM, c2, kinv, lane);
-  weights_pv_32<C, PREFETCH>(S, Vs, kb0, O, lane, knext, Ks, kb_next);
+  weights_pv_32<C, PREFETCH, ZERO>(S, Vs, kb0, O, lane, knext, Ks, kb_next);
 }
 
 // The weights exp2(t) of one 32-key step (t = c2*s - M per element, -inf for no weight),
@@ -951,27 +951,30 @@ __device__ __forceinline__ void weights_32(const f32x4_t (&S)[2][C::QB], u32x4_t
 
 // O^T += V^T.P^T for one 32-key step, with the row sums alongside (an MFMA of the rounded
 // weights against a block of ones), as one matrix burst at raised issue priority.
-template <class C>
+// ZERO: the first products of an item, on zero accumulators (O need not be initialised).
+template <class C, bool ZERO = false>
 __device__ __forceinline__ void pv_32(const VFrag<C>& V, const u32x4_t (&W)[C::QB], f32x4_t (&O)[C::NACC][C::QB]) {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
-      O[db][qb] = mma32<C::E>(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), O[db][qb]);
+      O[db][qb] = mma32<C::E>(V.a[db], __builtin_bit_cast(bf16x8_t, W[qb]), ZERO ? zero : O[db][qb]);
   const u32x4_t ones = {kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>, kOnes2<C::E>};
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb)
-    O[C::NDB][qb] = mma32<C::E>(__builtin_bit_cast(bf16x8_t, ones), __builtin_bit_cast(bf16x8_t, W[qb]), O[C::NDB][qb]);
+    O[C::NDB][qb] = mma32<C::E>(__builtin_bit_cast(bf16x8_t, ones), __builtin_bit_cast(bf16x8_t, W[qb]),
+                                ZERO ? zero : O[C::NDB][qb]);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // The weights of one 32-key step and O^T += V^T.P^T with the row sums alongside.
-template <class C, bool PREFETCH>
+template <class C, bool PREFETCH, bool ZERO>
 __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], const __bf16* Vs, int kb0,
                                               f32x4_t (&O)[C::NACC][C::QB], int lane, KFrag<C>* knext,
                                               const __bf16* Ks, int kb_next) {
@@ -985,10 +988,11 @@ __device__ __forceinline__ void weights_pv_32(const f32x4_t (&S)[2][C::QB], cons
   if constexpr (PREFETCH) load_k<C>(*knext, Ks, kb_next, lane);  // the next step's K, same tile
   u32x4_t W[C::QB];
   weights_32<C>(S, W);
-  pv_32<C>(V, W, O);
+  pv_32<C, ZERO>(V, W, O);
 }
 
 // One 32-key step [kb0, kb0 + 32) of the LDS tile: operand reads, both products, softmax.
+// FIRST also means the first value products of the item (O is set, not accumulated).
 template <class C, bool FIRST>
 __device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int kb0, int kinv,
                                         const bf16x8_t (&Q)[C::QB][C::NK32], const s16x4_t (&QT)[C::QB],
@@ -1008,7 +1012,7 @@ __device__ __forceinline__ void step_32(const __bf16* Ks, const __bf16* Vs, int 
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  softmax_pv_32<C, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
+  softmax_pv_32<C, FIRST, false, FIRST>(S, Vs, kb0, O, negM, c2, kinv, lane);
 }
 
 // One 32-key step whose V^T operands are read together with its K operands, before the
@@ -1087,6 +1091,7 @@ __device__ __forceinline__ void load_q16(bf16x8_t (&Q)[C::QB][C::NK32], s16x4_t 
                                          const __bf16* __restrict__ q, int row0, int qend, int head, int n_heads,
                                          int negate, int lane) {
   const int g = lane >> 4, c = lane & 15;
+  const unsigned nmask = negate ? 0x80008000u : 0u;  // wave-uniform: one xor per register, no select
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = min(row0 + qb * 16 + c, qend - 1);
@@ -1094,12 +1099,12 @@ __device__ __forceinline__ void load_q16(bf16x8_t (&Q)[C::QB][C::NK32], s16x4_t 
 #pragma unroll
     for (int ks = 0; ks < C::NK32; ++ks) {
       u32x4_t w = ld16(qrow + ks * 32 + 8 * g);
-      if (negate) w ^= 0x80008000u;
+      w ^= nmask;
       Q[qb][ks] = __builtin_bit_cast(bf16x8_t, w);
     }
     u32x2_t t = {0u, 0u};
     if (C::TAIL && C::NK32 * 32 + 4 * g < C::D) t = *reinterpret_cast<const u32x2_t*>(qrow + C::NK32 * 32 + 4 * g);
-    if (negate) t ^= 0x80008000u;
+    t ^= nmask;
     QT[qb] = __builtin_bit_cast(s16x4_t, t);
   }
 }
@@ -1181,11 +1186,7 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   s16x4_t QT[C::QB];
   load_q16<C>(Q, QT, q, row0, qend, item.head, n_heads, negate, lane);
 
-  f32x4_t O[C::NACC][C::QB];
-#pragma unroll
-  for (int db = 0; db < C::NACC; ++db)
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) O[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t O[C::NACC][C::QB];  // set by the first step's value products
   float negM[C::QB];
 
   // tile 0: the first step with a key in the sequence sets the exponent offsets

@@ -554,9 +554,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 // bf16 inputs: direct HBM->LDS staging, v_mfma_f32_16x16x32_bf16 for both products.
 //
 // LDS layout of one stage (one BN-key tile):
-//   K: [BN][KCH chunks of 16 B]  -- row stride KCH*4 words = 4*odd, so the 16-byte
-//      A-operand reads of 8 consecutive rows hit distinct banks.  Chunks past the
-//      head_dim hold a copy of real data (finite) and meet zero Q columns.
+//   K: [BN][KCH chunks of 16 B]  -- LDS has 64 banks of 4 bytes and serves a 16-byte read
+//      in passes of 32 lanes; the 32 lanes of one A-operand read cover 8 consecutive rows
+//      at 4 column chunks, so the row stride must put those 8 rows on distinct 16-byte bank
+//      groups that are also 32-byte aligned.  KCH = 2 (mod 4) does both (10 chunks for
+//      head_dim 64..80, 18 for 128); an odd stride costs about 4 extra cycles per read.  The
+//      8-byte reads of the 16-deep tail step still meet 2-way at KCH = 10, about 2 cycles
+//      per read, 2 reads per 32-key step.  Chunks past the head_dim hold a copy of real data
+//      (finite) and meet zero Q columns.
 //   V: [BN][VCH chunks of 16 B]  -- natural [key][d] order; read with the transposing
 //      ds_read_b64_tr_b16, whose 4-row x 32-byte footprint per 16 lanes is bank-conflict
 //      free with a row stride of 8 (mod 32) words.
@@ -583,7 +588,7 @@ struct Bf16Cfg {
   static constexpr int NDB = DV / 16;
   static constexpr int NACC = NDB + 1;         // plus one block for the row sums
   static constexpr int CH = D / 8;              // 16-byte chunks of a row in HBM
-  static constexpr int KCH = DK / 8 + 1;
+  static constexpr int KCH = (DK / 8 + 1) / 4 * 4 + 2;  // smallest >= DK / 8 with KCH % 4 == 2
   static constexpr int VCH = D <= 80 ? 10 : 18;
   static constexpr int KSTR = KCH * 8, VSTR = VCH * 8;  // elements
   static constexpr int K_BYTES = BN * KCH * 16, V_BYTES = BN * VCH * 16;
@@ -592,7 +597,7 @@ struct Bf16Cfg {
   static constexpr int LOADS = K_LOADS + V_LOADS;
   static_assert(D % 8 == 0 && BN % 64 == 0 && D - NK32 * 32 <= 16, "tile shape");
   static_assert(VCH * 8 >= DV && (VCH * 4) % 32 == 8, "V stride");
-  static_assert(((KCH * 4) / 4) % 2 == 1, "K stride");
+  static_assert(KCH * 8 >= DK && KCH % 4 == 2 && KCH - 4 < DK / 8, "K stride");
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

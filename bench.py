@@ -38,6 +38,7 @@ METRIC = "attention TFLOP/s (4*S^2*D*H) at S=912,D=80 and packed varlen; % bf16 
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (and f16) MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4       # the engine clock of the peak figures
 HEADLINE = "packed-varlen-8"
 FAMILY = ("tiny-64", "vit-196", "page-912", "packed-varlen-8", "long-16384")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -200,6 +201,170 @@ def committed_counters(name: str):
     return rec
 
 
+# The rocprofv3 runs behind profiles/attn_fwd_<workload>.md, run from the repository root (one
+# process each): a kernel trace of the timed bench command, then counter passes of a short bench
+# run (same settle rule, fewer launches), the last two with a plain copy of known size after the
+# attention launches to calibrate the HBM byte counters.
+PMC_PASSES = {
+    "p1": ["SQ_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU",
+           "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
+    "p2": ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY",
+           "SQ_INSTS_VALU_TRANS_F32", "SQ_INST_LEVEL_LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY"],
+    "p3": ["FETCH_SIZE"],
+    "p4": ["WRITE_SIZE"],
+}
+COPY_MIB = 256
+
+
+def profile_commands(name: str, out: str = "gpurun_out/prof") -> list:
+    """Shell commands (repository root as working directory) that write the raw rocprofv3 output
+    that --summarize-profiles reads: <out>/<workload>/<run>/run_*.csv and <out>/<workload>/<run>.json."""
+    base = f"python3 bench.py --workload {name} --no-secondary --no-cpu-baseline"
+    short = f"{base} --steps 20 --warmup 2 --settle-ms 20"
+    d = f"{out}/{name}"
+    cmds = [f"mkdir -p {d}",
+            f"TMPDIR=/tmp timeout -s KILL 300 rocprofv3 --kernel-trace --stats --output-format csv -d {d}/kt -o run "
+            f"-- {base} > {d}/kt.json"]
+    for run, ctrs in PMC_PASSES.items():
+        extra = f" --copy-calibration-mib {COPY_MIB}" if run in ("p3", "p4") else ""
+        cmds.append(f"TMPDIR=/tmp timeout -s KILL 300 rocprofv3 --pmc {' '.join(ctrs)} --output-format csv "
+                    f"-d {d}/{run} -o run -- {short}{extra} > {d}/{run}.json")
+    return cmds
+
+
+def _read_csv(path: str) -> list:
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(root: str, name: str) -> dict:
+    """Reads the rocprofv3 output of profile_commands(name) under `root` and writes
+    profiles/attn_fwd_<name>_counters.json and profiles/attn_fwd_<name>.md.  The averages are
+    over the timed launches only (the last `steps` attention dispatches of each run)."""
+    import statistics
+
+    from vision_transformer_attention_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    d = os.path.join(root, name)
+    is_attn = lambda r: "attn_fwd" in r["Kernel_Name"]
+    bench = {run: json.load(open(os.path.join(d, f"{run}.json"))) for run in ["kt", *PMC_PASSES]}
+    agent = next(r for r in _read_csv(os.path.join(d, "kt", "run_agent_info.csv")) if r["Agent_Type"] == "GPU")
+    n_simd, n_se = int(agent["Simd_Count"]), int(agent["Array_Count"])
+
+    # kernel trace: the timed launches are the last `steps` dispatches of the attention kernel
+    kt = sorted((r for r in _read_csv(os.path.join(d, "kt", "run_kernel_trace.csv")) if is_attn(r)),
+                key=lambda r: int(r["Dispatch_Id"]))
+    steps = bench["kt"]["steps"]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in kt]
+    timed = durs[-steps:]
+    trace = {"dispatches": len(durs), "timed": len(timed), "mean_us": statistics.fmean(timed),
+             "min_us": min(timed), "max_us": max(timed), "all_mean_us": statistics.fmean(durs),
+             "kernel": kt[-1]["Kernel_Name"], "bench_us": bench["kt"]["ms_per_step"] * 1e3,
+             "bench_cold_us": (bench["kt"].get("cold_ms_per_step") or 0.0) * 1e3}
+    stats_rows = _read_csv(os.path.join(d, "kt", "run_kernel_stats.csv"))
+
+    # counter passes: per-dispatch values of the last `steps` attention dispatches
+    ctr, spread, dur_ns, calib = {}, {}, {}, {}
+    for run, names in PMC_PASSES.items():
+        rows = _read_csv(os.path.join(d, run, "run_counter_collection.csv"))
+        by = {}
+        for r in rows:
+            by.setdefault(int(r["Dispatch_Id"]), []).append(r)
+        ids = sorted(i for i, rs in by.items() if is_attn(rs[0]))
+        n = bench[run]["steps"]
+        use = ids[-n:]
+        for c in names:
+            vals = [sum(float(r["Counter_Value"]) for r in by[i] if r["Counter_Name"] == c) for i in use]
+            ctr[c] = statistics.fmean(vals)
+            spread[c] = (min(vals), max(vals))
+        dur_ns[run] = statistics.fmean(int(by[i][0]["End_Timestamp"]) - int(by[i][0]["Start_Timestamp"]) for i in use)
+        if run in ("p3", "p4"):  # the copy dispatches after the last attention launch
+            copies = [i for i in by if i > ids[-1] and "copy" in by[i][0]["Kernel_Name"].lower()]
+            calib[names[0]] = (sum(float(r["Counter_Value"]) for i in copies for r in by[i]
+                                   if r["Counter_Name"] == names[0]), len(copies), by[copies[0]][0]["Kernel_Name"])
+    copy_kib = COPY_MIB * 1024.0
+    f_scale = copy_kib / calib["FETCH_SIZE"][0]
+    w_scale = copy_kib / calib["WRITE_SIZE"][0]
+    rd = ctr["FETCH_SIZE"] * f_scale * 1024.0
+    wr = ctr["WRITE_SIZE"] * w_scale * 1024.0
+    es = 4 if w.dtype == "f32" else 2
+    q_rows = w.total_tokens * w.n_heads * w.head_dim
+    kv_rows = w.total_tokens * w.kv_heads * w.head_dim
+    alg = (2 * q_rows + 2 * kv_rows) * es
+    clock_ghz = ctr["SQ_CYCLES"] / n_se / dur_ns["p1"]
+    # busy cycles of the matrix pipes over the counter run's own dispatch time at the 2.4 GHz of
+    # the peak figures (a lower bound on the fraction when the clock ran lower)
+    mfma_busy = ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * dur_ns["p1"] * PEAK_CLOCK_GHZ)
+    rec = {
+        "kernel": trace["kernel"], "workload": name, "source_sha256": kernel_sha(),
+        "trace_mean_us": trace["mean_us"], "trace": trace,
+        "counters_mean_per_dispatch": ctr,
+        "hbm_bytes_per_launch": rd + wr, "hbm_read_bytes": rd, "hbm_write_bytes": wr,
+        "algorithmic_bytes": alg, "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_gbs": (rd + wr) / (trace["mean_us"] * 1e3),
+        "mfma_busy": mfma_busy, "counter_run_clock_ghz": clock_ghz,
+        "lds_conflict_cycles_per_lds_inst": ctr["SQ_LDS_BANK_CONFLICT"] / ctr["SQ_INSTS_LDS"],
+        "valu_per_mfma": ctr["SQ_INSTS_VALU"] / ctr["SQ_INSTS_MFMA"],
+        "profile": f"attn_fwd_{name}.md",
+    }
+    with open(os.path.join(PROFILES, f"attn_fwd_{name}_counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+    tf = w.flops / (trace["mean_us"] * 1e-6) / 1e12
+    lines = [
+        f"# Attention kernel on {name} ({len(w.lengths)} sequence(s), {w.total_tokens:,} tokens, {w.n_heads} heads "
+        f"of {w.head_dim}, {w.dtype})", "",
+        f"Kernel source sha256: `{rec['source_sha256']}`", "",
+        "## Commands (repository root, one MI355X; written by `bench.py --profile-commands "
+        f"{name}`, summarised by `bench.py --summarize-profiles gpurun_out/prof --workload {name}`)", "", "```",
+        *profile_commands(name), "```", "",
+        "## Kernel trace (`kt`)", "",
+        f"Kernel: `{trace['kernel']}`", "",
+        f"- {trace['dispatches']} dispatches (one set-up call, {bench['kt']['warmup']} cold warm-up launches, "
+        f"the settle launches, {steps} timed launches).",
+        f"- Timed launches: mean {trace['mean_us']:.2f} us (min {trace['min_us']:.2f}, max {trace['max_us']:.2f}), "
+        f"{tf:.1f} TFLOP/s, {tf / peak_of(w.dtype):.1%} of the dense peak.",
+        f"- bench.py in the same profiled run: {trace['bench_us']:.2f} us per launch (HIP events around the "
+        f"timed launches); cold warm-up {trace['bench_cold_us']:.2f} us per launch.",
+        f"- Mean over every dispatch of the run: {trace['all_mean_us']:.2f} us.", "",
+        "`--stats` rows:", "", "```",
+        *[f"{r['Name'][:90]}: calls {r['Calls']}, average {float(r['AverageNs']) / 1e3:.2f} us, "
+          f"min {float(r['MinNs']) / 1e3:.2f}, max {float(r['MaxNs']) / 1e3:.2f}" for r in stats_rows],
+        "```", "",
+        f"## Counters (mean per timed dispatch of the counter runs: last {bench['p1']['steps']} of each)", "",
+        f"Counter runs serialise dispatches; their mean dispatch took {dur_ns['p1'] / 1e3:.2f} us in pass p1"
+        + (f", and SQ_CYCLES / ({n_se} shader arrays x duration) puts the shader clock at {clock_ghz:.2f} GHz"
+           if dur_ns["p1"] > 1e5 else " (too short for a clock estimate from SQ_CYCLES, which then also counts "
+           "cycles outside the dispatch)")
+        + ".  The instruction, byte and conflict counts do not depend on the clock.", "",
+        "| counter | mean | min | max |", "|---|---|---|---|",
+        *[f"| {c} | {v:,.0f} | {spread[c][0]:,.0f} | {spread[c][1]:,.0f} |" for c, v in sorted(ctr.items())], "",
+        "## HBM traffic", "",
+        f"Calibration: one {COPY_MIB} MiB device-to-device copy after the attention launches "
+        f"({calib['FETCH_SIZE'][1]} dispatch(es) of `{calib['FETCH_SIZE'][2][:60]}`) reads FETCH_SIZE "
+        f"{calib['FETCH_SIZE'][0]:,.1f} KiB and WRITE_SIZE {calib['WRITE_SIZE'][0]:,.1f} KiB in total against "
+        f"{copy_kib:,.0f} KiB moved each way: scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+        f"Per attention launch: {rd / 1e6:.1f} MB read + {wr / 1e6:.1f} MB written = {(rd + wr) / 1e6:.1f} MB "
+        f"against {alg / 1e6:.1f} MB of algorithmic bytes (Q, K, V read once, O written once): "
+        f"{(rd + wr) / alg:.2f}x; {rec['hbm_gbs']:.0f} GB/s over the trace mean "
+        f"({rec['hbm_gbs'] / HBM_PEAK_GBS:.1%} of {HBM_PEAK_GBS:.0f}).", "",
+        "## Derived", "",
+        f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / ({n_simd} SIMDs x {dur_ns['p1'] / 1e3:.2f} us x "
+        f"{PEAK_CLOCK_GHZ} GHz) = {mfma_busy:.1%} (the pipes' busy share of the dispatch).",
+        f"- VALU instructions per MFMA instruction: {rec['valu_per_mfma']:.2f}; transcendental (exp2) "
+        f"{ctr['SQ_INSTS_VALU_TRANS_F32']:,.0f} per dispatch.",
+        f"- LDS bank-conflict cycles per LDS instruction: {rec['lds_conflict_cycles_per_lds_inst']:.3f}.",
+        f"- VALU/MFMA co-issue: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES = "
+        f"{ctr['SQ_VALU_MFMA_COEXEC_CYCLES'] / ctr['SQ_VALU_MFMA_BUSY_CYCLES']:.1%}.",
+        "",
+    ]
+    with open(os.path.join(PROFILES, f"attn_fwd_{name}.md"), "w") as f:
+        f.write("\n".join(lines))
+    return rec
+
+
 def cpu_leg(name: str, gpu_outputs: dict, target_s: float = 10.0, one_core_s: float = 8.0):
     """The float64 oracle: timed on the host cores (all, then one) on a bounded sample of the
     headline workload's query rows, and compared with each workload's GPU output on a bounded
@@ -292,7 +457,20 @@ def main():
                     help="time the qkv prologue (split, per-head RMS norm, rope) instead of the attention")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--profile-commands", action="store_true",
+                    help="print the rocprofv3 commands behind profiles/attn_fwd_<workload>.md and exit")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/attn_fwd_<workload>.md and _counters.json from the rocprofv3 output "
+                         "that --profile-commands wrote under DIR, and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.workload)))
+        return
+    if args.summarize_profiles:
+        rec = summarize_profiles(args.summarize_profiles, args.workload)
+        log(f"[bench] wrote profiles/attn_fwd_{args.workload}.md: trace mean {rec['trace_mean_us']:.2f} us, "
+            f"MFMA busy {rec['mfma_busy']:.1%}, HBM {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this attention path is a single-GPU "
               f"build; DESIGN.md describes how it would shard.", file=sys.stderr)

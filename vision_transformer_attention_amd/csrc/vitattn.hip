@@ -559,9 +559,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 //      at 4 column chunks, so the row stride must put those 8 rows on distinct 16-byte bank
 //      groups that are also 32-byte aligned.  KCH = 2 (mod 4) does both (10 chunks for
 //      head_dim 64..80, 18 for 128); an odd stride costs about 4 extra cycles per read.  The
-//      8-byte reads of the 16-deep tail step still meet 2-way at KCH = 10, about 2 cycles
-//      per read, 2 reads per 32-key step.  Chunks past the head_dim hold a copy of real data
-//      (finite) and meet zero Q columns.
+//      8-byte reads of the 16-deep tail step (head_dim 72, 80: chunks TCH and TCH + 1) take 16
+//      rows x one chunk per pass, which a stride of 10 chunks puts 2-way on rows c and c + 8;
+//      rows with bit 3 set therefore hold those two chunks swapped (the tail swizzle).  Chunks
+//      past the head_dim hold a copy of real data (finite) and meet zero Q columns.
 //   V: [BN][VCH chunks of 16 B]  -- natural [key][d] order; read with the transposing
 //      ds_read_b64_tr_b16, whose 4-row x 32-byte footprint per 16 lanes is bank-conflict
 //      free with a row stride of 8 (mod 32) words.
@@ -589,6 +590,7 @@ struct Bf16Cfg {
   static constexpr int NACC = NDB + 1;         // plus one block for the row sums
   static constexpr int CH = D / 8;              // 16-byte chunks of a row in HBM
   static constexpr int KCH = (DK / 8 + 1) / 4 * 4 + 2;  // smallest >= DK / 8 with KCH % 4 == 2
+  static constexpr int TCH = NK32 * 4;                   // first chunk of the 16-deep tail
   static constexpr int VCH = D <= 80 ? 10 : 18;
   static constexpr int KSTR = KCH * 8, VSTR = VCH * 8;  // elements
   static constexpr int K_BYTES = BN * KCH * 16, V_BYTES = BN * VCH * 16;
@@ -598,6 +600,7 @@ struct Bf16Cfg {
   static_assert(D % 8 == 0 && BN % 64 == 0 && D - NK32 * 32 <= 16, "tile shape");
   static_assert(VCH * 8 >= DV && (VCH * 4) % 32 == 8, "V stride");
   static_assert(KCH * 8 >= DK && KCH % 4 == 2 && KCH - 4 < DK / 8, "K stride");
+  static_assert(!TAIL || TCH + 2 == KCH, "the tail swizzle swaps the last two chunks of a K row");
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -645,7 +648,9 @@ struct Dma {
     constexpr int per = IS_K ? C::KCH : C::VCH;
     const unsigned z = (unsigned)(s * 64 + lane);
     const int row = max((int)(z / per), lead) - lead;  // division by a constant
-    const int ch = min((int)(z % per), C::CH - 1);
+    int ch = (int)(z % per);
+    if constexpr (IS_K && C::TAIL) ch ^= (int)(ch >= C::TCH && ((z / per) & 8u) != 0u);  // tail swizzle
+    ch = min(ch, C::CH - 1);
     return (unsigned)row * row_bytes + (unsigned)ch * 16u;
   }
 
@@ -794,7 +799,12 @@ __device__ __forceinline__ void load_k(KFrag<C>& f, const __bf16* Ks, int kb0, i
     const __bf16* row = Ks + (kb0 + kb * 16 + c) * C::KSTR;
 #pragma unroll
     for (int ks = 0; ks < C::NK32; ++ks) f.a[kb][ks] = *reinterpret_cast<const bf16x8_t*>(row + ks * 32 + 8 * g);
-    if constexpr (C::TAIL) f.t[kb] = *reinterpret_cast<const s16x4_t*>(row + C::NK32 * 32 + 4 * g);
+    if constexpr (C::TAIL) {
+      // tail swizzle: rows with bit 3 set hold the two tail chunks swapped
+      int t_off = (4 * g) ^ (c & 8);
+      if (kb) asm volatile("" : "+v"(t_off));  // two separate 8-byte reads, not one paired read
+      f.t[kb] = *reinterpret_cast<const s16x4_t*>(row + C::NK32 * 32 + t_off);
+    }
   }
 }
 

@@ -82,6 +82,11 @@ typedef enum {
  * n_heads : > 0.  head_dim : 64, 72, 80 or 128.
  * scale   : finite; multiplies q.k before the softmax (1/sqrt(head_dim) for a
  *           standard ViT; 1.0 is valid).
+ * Inputs  : q, k and v hold finite values (no NaN, no infinity).  This is a
+ *           precondition the library does not check: the kernels are built
+ *           without NaN handling in their max and min operations, so a
+ *           non-finite input gives unspecified (but in-bounds) output rows for
+ *           the sequences and heads that read it.
  * dtype   : a vitattn_dtype_t.
  * stream  : HIP stream to enqueue on (0 = the legacy default stream).
  *

@@ -181,8 +181,13 @@ def time_prologue(name: str, steps: int, warmup: int, settle_ms: float):
 
 
 def kernel_sha() -> str:
+    """Fingerprint of the kernel binary's inputs: the HIP source and the hipcc flags."""
+    import __graft_entry__
+    h = hashlib.sha256()
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+        h.update(f.read())
+    h.update(" ".join(__graft_entry__.HIP_FLAGS).encode())
+    return h.hexdigest()
 
 
 def committed_counters(name: str):
@@ -202,9 +207,9 @@ def committed_counters(name: str):
 
 
 # The rocprofv3 runs behind profiles/attn_fwd_<workload>.md, run from the repository root (one
-# process each): a kernel trace of the timed bench command, then counter passes of a short bench
-# run (same settle rule, fewer launches), the last two with a plain copy of known size after the
-# attention launches to calibrate the HBM byte counters.
+# process each): a kernel trace of the timed bench command, then counter passes of the same
+# command with 20 timed launches (the same warm-up and settle before them), the last two with a
+# plain copy of known size after the attention launches to calibrate the HBM byte counters.
 PMC_PASSES = {
     "p1": ["SQ_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU",
            "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
@@ -220,7 +225,7 @@ def profile_commands(name: str, out: str = "gpurun_out/prof") -> list:
     """Shell commands (repository root as working directory) that write the raw rocprofv3 output
     that --summarize-profiles reads: <out>/<workload>/<run>/run_*.csv and <out>/<workload>/<run>.json."""
     base = f"python3 bench.py --workload {name} --no-secondary --no-cpu-baseline"
-    short = f"{base} --steps 20 --warmup 2 --settle-ms 20"
+    short = f"{base} --steps 20"  # the same warm-up and settle as the trace run, fewer timed launches
     d = f"{out}/{name}"
     cmds = [f"mkdir -p {d}",
             f"TMPDIR=/tmp timeout -s KILL 300 rocprofv3 --kernel-trace --stats --output-format csv -d {d}/kt -o run "
@@ -316,7 +321,7 @@ def summarize_profiles(root: str, name: str) -> dict:
     lines = [
         f"# Attention kernel on {name} ({len(w.lengths)} sequence(s), {w.total_tokens:,} tokens, {w.n_heads} heads "
         f"of {w.head_dim}, {w.dtype})", "",
-        f"Kernel source sha256: `{rec['source_sha256']}`", "",
+        f"Kernel fingerprint (sha256 of the HIP source and the hipcc flags): `{rec['source_sha256']}`", "",
         "## Commands (repository root, one MI355X; written by `bench.py --profile-commands "
         f"{name}`, summarised by `bench.py --summarize-profiles gpurun_out/prof --workload {name}`)", "", "```",
         *profile_commands(name), "```", "",

@@ -77,16 +77,17 @@ typedef enum {
  *           rows [cu_seqlens[s], cu_seqlens[s+1]).  Zero-length sequences are
  *           allowed and produce nothing.  This is a precondition the library
  *           does not check (it never reads device memory on the host); the
- *           Python binding checks it.
+ *           Python binding checks it when the array is on the host or when
+ *           asked to.
  * n_seqs  : number of sequences (images), >= 0.  0 enqueues nothing.
  * n_heads : > 0.  head_dim : 64, 72, 80 or 128.
  * scale   : finite; multiplies q.k before the softmax (1/sqrt(head_dim) for a
  *           standard ViT; 1.0 is valid).
  * Inputs  : q, k and v hold finite values (no NaN, no infinity).  This is a
- *           precondition the library does not check: the kernels are built
- *           without NaN handling in their max and min operations, so a
- *           non-finite input gives unspecified (but in-bounds) output rows for
- *           the sequences and heads that read it.
+ *           precondition the library does not check (it never reads device
+ *           memory on the host); a non-finite input gives unspecified (but
+ *           in-bounds) output rows for the sequences and heads that read it,
+ *           NaN rows in practice.
  * dtype   : a vitattn_dtype_t.
  * stream  : HIP stream to enqueue on (0 = the legacy default stream).
  *

@@ -243,7 +243,7 @@ def _read_csv(path: str) -> list:
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(root: str, name: str) -> dict:
+def summarize_profiles(root: str, name: str, out_dir: str = PROFILES) -> dict:
     """Reads the rocprofv3 output of profile_commands(name) under `root` and writes
     profiles/attn_fwd_<name>_counters.json and profiles/attn_fwd_<name>.md.  The averages are
     over the timed launches only (the last `steps` attention dispatches of each run)."""
@@ -314,7 +314,7 @@ def summarize_profiles(root: str, name: str) -> dict:
         "valu_per_mfma": ctr["SQ_INSTS_VALU"] / ctr["SQ_INSTS_MFMA"],
         "profile": f"attn_fwd_{name}.md",
     }
-    with open(os.path.join(PROFILES, f"attn_fwd_{name}_counters.json"), "w") as f:
+    with open(os.path.join(out_dir, f"attn_fwd_{name}_counters.json"), "w") as f:
         json.dump(rec, f, indent=1)
 
     tf = w.flops / (trace["mean_us"] * 1e-6) / 1e12
@@ -365,7 +365,7 @@ def summarize_profiles(root: str, name: str) -> dict:
         f"{ctr['SQ_VALU_MFMA_COEXEC_CYCLES'] / ctr['SQ_VALU_MFMA_BUSY_CYCLES']:.1%}.",
         "",
     ]
-    with open(os.path.join(PROFILES, f"attn_fwd_{name}.md"), "w") as f:
+    with open(os.path.join(out_dir, f"attn_fwd_{name}.md"), "w") as f:
         f.write("\n".join(lines))
     return rec
 

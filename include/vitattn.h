@@ -85,9 +85,10 @@ typedef enum {
  *           standard ViT; 1.0 is valid).
  * Inputs  : q, k and v hold finite values (no NaN, no infinity).  This is a
  *           precondition the library does not check (it never reads device
- *           memory on the host); a non-finite input gives unspecified (but
- *           in-bounds) output rows for the sequences and heads that read it,
- *           NaN rows in practice.
+ *           memory on the host): the kernels are built without NaN handling
+ *           in their max and min operations, so a non-finite input gives
+ *           unspecified (but in-bounds) output rows for the sequences and
+ *           heads that read it.
  * dtype   : a vitattn_dtype_t.
  * stream  : HIP stream to enqueue on (0 = the legacy default stream).
  *

@@ -154,8 +154,9 @@ def fwd(q, k, v, cu_seqlens, scale: float | None = None, out=None, check_cu: boo
     {64, 72, 80, 128}; k, v: the same dtype, ``[T, Hkv, D]`` with Hkv dividing H
     (Hkv < H is grouped-query attention: query head h uses K/V head
     ``h // (H // Hkv)``).  The inputs must be finite (not checked: that would read
-    them back); a NaN or infinity in q, k or v, or a score that overflows float32,
-    gives unspecified output rows for the sequences and heads that read it.  cu_seqlens: int32
+    them back): the kernels are built without NaN handling in max/min, and a NaN or
+    infinity in q, k or v, or a score that overflows float32, gives unspecified
+    output rows for the sequences and heads that read it.  cu_seqlens: int32
     ``[n_seqs + 1]`` prefix array (0, non-decreasing, ending at T).  On q's device it
     is passed to the kernel as it is, and the call neither waits for the device nor
     allocates anything beyond ``out`` (so it can be captured into a HIP graph when

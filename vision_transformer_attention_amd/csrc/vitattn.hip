@@ -693,7 +693,8 @@ struct Dma {
   // multiple of BN) repeat key0.  The loads go through buffer resources based at key0 and
   // bounded by the last key row of the sequence, so a lane reads at most that far (an offset
   // past it would read zeros, never memory outside the sequence).
-  template <bool LEAD>
+  // PARTS: which loads of the wave to issue (1: the K area's, 2: the V area's, 3: both).
+  template <bool LEAD, int PARTS = 3>
   static __device__ __forceinline__ void issue(const Src& sr, lds_u8_t* buf, int lead, unsigned row_bytes,
                                                const unsigned (&off)[PER_WAVE], int wave, int lane) {
     const int n_rec = (int)(sr.extent < 0x7fffffffll ? sr.extent : 0x7fffffffll);
@@ -705,13 +706,13 @@ struct Dma {
     int ln = lane;
     if constexpr (LEAD) asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) {
+    for (int i = 0; i < ((PARTS & 1) ? KPW : 0); ++i) {
       const int s = slot(wave, i, C::K_LOADS);
       const unsigned o = LEAD ? lane_offset<true>(s, ln, lead, row_bytes) : off[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + s * 1024), 16, o, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < VPW; ++i) {
+    for (int i = 0; i < ((PARTS & 2) ? VPW : 0); ++i) {
       const int s = slot(wave, i, C::V_LOADS);
       const unsigned o = LEAD ? lane_offset<false>(s, ln, lead, row_bytes) : off[KPW + i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + C::K_BYTES + s * 1024), 16, o, 0, 0, 0);
@@ -1222,10 +1223,15 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
   }
   // every later tile: two full steps; the second step's K operands are read while the first
   // step's exponentials run
+  // The next tile's loads go out in two halves, the K area's after the barrier and the V
+  // area's between the two steps, so that the workgroups of a CU do not all queue their whole
+  // tile at the vector-memory unit at once.
   for (int t = 1; t < ntiles; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile t has landed
     __syncthreads();  // every wave's has; buffer (t+1)&1 is no longer read
-    if (t + 1 < ntiles) issue_next(t + 1);
+    const bool more = t + 1 < ntiles;
+    lds_u8_t* nbuf = stage + ((t + 1) & 1) * C::STAGE_BYTES;
+    if (more) Dma<C>::template issue<false, 1>(sr, nbuf, 0, row_bytes, dma_off, wave, lane);
     const lds_u8_t* buf = stage + (t & 1) * C::STAGE_BYTES;
     const __bf16* Ks = (const __bf16*)(buf);
     const __bf16* Vs = (const __bf16*)(buf + C::K_BYTES);
@@ -1233,11 +1239,14 @@ __device__ __forceinline__ void run_item(const Item& item, const __bf16* __restr
     load_k<C>(k0, Ks, 0, lane);
     if constexpr (C::QB <= kEarlyVMaxQB) {
       step_32k_ev<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      if (more) Dma<C>::template issue<false, 2>(sr, nbuf, 0, row_bytes, dma_off, wave, lane);
       step_32k_ev<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
     } else {
       step_32k<C, true>(k0, k1, Ks, Vs, 0, Q, QT, O, negM, c2, lane);
+      if (more) Dma<C>::template issue<false, 2>(sr, nbuf, 0, row_bytes, dma_off, wave, lane);
       step_32k<C, false>(k1, k0, Ks, Vs, C::KSUB, Q, QT, O, negM, c2, lane);
     }
+    if (more) sr.advance(row_bytes);
   }
 
   store_o16<C>(o, O, row0, qend, item.head, n_heads, lane);

@@ -254,7 +254,11 @@ def summarize_profiles(root: str, name: str, out_dir: str = PROFILES) -> dict:
     w = inputs.WORKLOADS[name]
     d = os.path.join(root, name)
     is_attn = lambda r: "attn_fwd" in r["Kernel_Name"]
-    bench = {run: json.load(open(os.path.join(d, f"{run}.json"))) for run in ["kt", *PMC_PASSES]}
+    def bench_line(run):  # the JSON line that run's bench.py printed (its last line)
+        with open(os.path.join(d, f"{run}.json")) as f:
+            return json.loads(f.read().strip().splitlines()[-1])
+
+    bench = {run: bench_line(run) for run in ["kt", *PMC_PASSES]}
     agent = next(r for r in _read_csv(os.path.join(d, "kt", "run_agent_info.csv")) if r["Agent_Type"] == "GPU")
     n_simd, n_se = int(agent["Simd_Count"]), int(agent["Array_Count"])
 

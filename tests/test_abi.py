@@ -218,3 +218,16 @@ def test_binding_dtype_codes():
     for bad in ((torch.float32, torch.bfloat16), (torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16)):
         with pytest.raises(TypeError):
             b._call_code(*bad)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # no CPU fallback: without the HIP library every entry point of the binding raises
+    import torch
+    with pytest.raises(binding.VitattnError):
+        binding.load_library(str(tmp_path / "libvitattn.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "libvitattn.so"))
+    q = torch.zeros(4, 2, 80, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(binding.VitattnError):
+        vta.fwd(q, q, q, cu)

@@ -1654,18 +1654,30 @@ __global__ __launch_bounds__(CA::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const unsigned row_bytes = (unsigned)n_kv_heads * CA::D * 2u;  // one K/V row
   const int kv_group = n_heads / n_kv_heads;                       // query heads per K/V head
 
-  // Items in longest-first order are dealt out in rounds of G, alternating direction to
-  // even out the load.  Within a round of m items, XCD x takes the contiguous run
-  // [x*m/8, (x+1)*m/8) (items of one sequence and head share K/V in that XCD's L2), so a
-  // last, partial round still spreads over all XCDs.
-  for (int round = 0;; ++round) {
-    const int base = round * G;
+  // Items in longest-first order are dealt out in rounds ("tiers") of R = G/2 items, one per
+  // CU.  The hardware places workgroups b and b + G/2 on one CU, and the older of the two
+  // (b < G/2) issues first: paired, it runs about 1.45 times as fast as the younger one.  So
+  // even tiers go to the older halves of the CU pairs and odd tiers to the younger halves, with
+  // the direction reversed every second tier (tier 2 pairs the largest items of the older
+  // halves' first tier with the smallest of their second): the older halves get the larger
+  // items, and the CU totals stay even.  Within a tier of m items, XCD x takes the contiguous
+  // run [x*m/8, (x+1)*m/8) (items of one sequence and head share K/V in that XCD's L2), so a
+  // last, partial tier still spreads over all XCDs.  Items that fit in one round of the
+  // grid (short images), and a grid that is not a multiple of 16, are dealt in rounds of the
+  // whole grid instead, alternating direction.
+  const bool tiered = (G & 15) == 0 && n_items > G;
+  const int R = tiered ? G >> 1 : G;                      // items per tier
+  const int half = tiered ? (blockIdx.x >= R ? 1 : 0) : 0;  // the younger half of a CU pair
+  const int xk = tiered ? (blockIdx.x - half * R) >> 3 : xj;  // position inside the XCD's run
+  for (int tier = half;; tier += tiered ? 2 : 1) {
+    const int base = tier * R;
     if (base >= n_items) break;
-    const int m = min(G, n_items - base);
+    const int m = min(R, n_items - base);
     const int lo = (xcd * m) >> 3, cnt = (((xcd + 1) * m) >> 3) - lo;
-    if (xj >= cnt) break;  // only the last round can leave a workgroup without an item
-    const int kk = lo + xj;
-    const int it = base + ((round & 1) ? m - 1 - kk : kk);
+    if (xk >= cnt) break;  // only the last tier can leave a workgroup without an item
+    const int kk = lo + xk;
+    const bool rev = tiered ? ((tier >> 1) & 1) : (tier & 1);
+    const int it = base + (rev ? m - 1 - kk : kk);
     Item item = levels ? map_item_levels(plan, levels, it, bm, n_heads) : map_item(plan, n_seqs, it, bm);
     item.a = __builtin_amdgcn_readfirstlane(item.a);
     item.b = __builtin_amdgcn_readfirstlane(item.b);

@@ -382,3 +382,30 @@ def test_float32_output_from_16_bit_inputs(dtype, head_dim):
 
 def test_float32_output_grouped_query_packed_sampled():
     check_workload(inputs.WORKLOADS["packed-varlen-8-gqa4"], full=False, out_dtype=torch.float32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("extra", [1, 9, 257, 263])
+def test_large_item_deal_around_one_round_of_the_grid(extra):
+    # Launches with more large items than one round of the grid are dealt in tiers of half the
+    # grid, alternately to the two halves of the CU pairs; G + extra items (one head, so an item
+    # is one 256-query block of an image) with every item checked at two rows.
+    from vision_transformer_attention_amd import binding
+    cfg = binding.kernel_config(80, torch.bfloat16)
+    grid, bm = cfg["grid"], cfg["block_m"]
+    rng = np.random.default_rng(500 + extra)
+    target = grid + extra
+    blocks = []
+    while sum(blocks) < target:
+        blocks.append(int(min(rng.integers(8, 40), target - sum(blocks))))
+    lengths = [b * bm - int(rng.integers(0, bm - 1)) for b in blocks]  # ragged last blocks
+    assert sum(-(-n // bm) for n in lengths) == target
+    w = inputs.custom(lengths, n_heads=1, head_dim=80, dtype=inputs.BF16, seed=77 + extra)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    rows = []
+    for s, n in enumerate(lengths):
+        for b in range(-(-n // bm)):
+            for off in ((7 * b) % 64, bm // 2 + (13 * b) % 64):
+                r = min(b * bm + off, n - 1)
+                rows.append(int(cu[s]) + r)
+    check_workload(w, full=False, rows=np.array(sorted(set(rows)), np.int64))
